@@ -1,0 +1,423 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each ``check_*`` takes the oracle module as its argument and raises
+AssertionError on a mismatch, so the same checks serve the real oracle
+(test_oracle_pins.py) and deliberately broken copies of it
+(test_oracle_mutants.py), which must each fail at least one check.
+
+What pins what
+--------------
+* printed worked example (NNX ALiBi-Style Attention, "A small example"):
+  bias sign and distance, slopes, non-causal softmax, weighted sum of V;
+* closed forms on T = 2 (offset sign, SSMax factor, lse, first causal row);
+* reductions to torch's scaled_dot_product_attention in fp64 on the CPU:
+  ALiBi (beta = 1, the textbook linear bias of "ALiBi: Attention with Linear
+  Biases", "Code"), NoPE (alpha = inf, and beta = 0), Gaussian (beta = 2,
+  built by multiplication) and square-root priors (beta = +-1/2, built with
+  sqrt / rsqrt), each with the SSMax factor pre-applied to q and the mask;
+* brute force in 40-digit mpmath arithmetic with explicit loops on T <= 6;
+* invariants: rows of P sum to 1, V = I gives P, V = 1 gives 1, first causal
+  row copies V_0, ALiBi weight-ratio law ("One fixed slope per head": every
+  extra unit of distance multiplies the weight ratio by exp(-slope));
+* decode equals the last prefill row and the brute force;
+* backward: central finite differences of sum(O * dO) for every input, and
+  the ALiBi closed form db/dalpha = m^2 |d| at beta = 1.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split()
+            vals[key] = float(val)
+    return vals
+
+
+def alibi_slopes(H):
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)])
+
+
+# ----------------------------------------------------------------------------------
+# worked example and closed forms
+# ----------------------------------------------------------------------------------
+
+def check_worked_example(orc):
+    g = read_golden("alibi_worked_example.txt")
+    H, T = int(g["heads"]), int(g["positions"])
+    m = alibi_slopes(H)
+    q = np.zeros((1, H, T, 1))
+    k = np.zeros((1, H, T, 1))
+    v = np.zeros((1, H, T, 1))
+    v[..., 1, 0] = 1.0
+    O, _ = orc.attn_fwd(q, k, v, 1.0 / m, np.ones(H), np.zeros(H), np.ones(H),
+                        causal=False, ssmax=False)
+    expected = 1.0 / (1.0 + np.exp(m))
+    _close(O[0, :, 0, 0], expected, 1e-15, "worked example, position 0 (closed form)")
+    _close(O[0, :, 1, 0], 1.0 - expected, 1e-15, "worked example, position 1 (closed form)")
+    _close(O[0, 0, :, 0], [g["head0_pos0"], g["head0_pos1"]], 5e-8, "worked example, printed head 0")
+
+
+def check_closed_form_offset_ssmax(orc):
+    """T = 2, causal, zero content, V = [0, 1], Gaussian prior beta = 2, alpha = 1, mu = -1/2.
+
+    b(d) = -(d + 1/2)^2: b(0) = -1/4, b(1) = -9/4.  Row 1 sees keys 0 (d = 1) and 1 (d = 0).
+    SSMax off: weight of key 1 = 1 / (1 + e^(b(1) - b(0))) = 1 / (1 + e^-2).
+    SSMax on, s = 1/2: c_1 = ln(2)/2, logit gap c_1 * 2 = ln 2, weight = 2/3 exactly;
+    lse_1 = -ln(2)/8 + ln(3/2).  Row 0 sees key 0 only: O_0 = V_0 = 0; with SSMax on
+    c_0 = s ln 1 = 0 so lse_0 = 0; with it off lse_0 = b(0) = -1/4.
+    """
+    q = np.zeros((1, 1, 2, 3))
+    k = np.zeros((1, 1, 2, 3))
+    v = np.zeros((1, 1, 2, 3))
+    v[0, 0, 1, :] = 1.0
+    a, be, mu = np.array([1.0]), np.array([2.0]), np.array([-0.5])
+    O, lse = orc.attn_fwd(q, k, v, a, be, mu, np.array([0.5]), causal=True, ssmax=False)
+    _close(O[0, 0, 1, 0], 1.0 / (1.0 + math.exp(-2.0)), 1e-15, "T=2 Gaussian, SSMax off")
+    _close(O[0, 0, 0, :], [0.0, 0.0, 0.0], 0.0, "T=2 first row")
+    _close(lse[0, 0, 0], -0.25, 1e-15, "T=2 lse row 0, SSMax off")
+    O, lse = orc.attn_fwd(q, k, v, a, be, mu, np.array([0.5]), causal=True, ssmax=True)
+    _close(O[0, 0, 1, 0], 2.0 / 3.0, 1e-15, "T=2 Gaussian, SSMax s=1/2")
+    _close(lse[0, 0, 1], -math.log(2.0) / 8.0 + math.log(1.5), 1e-15, "T=2 lse row 1, SSMax")
+    _close(lse[0, 0, 0], 0.0, 0.0, "T=2 lse row 0, SSMax (c_0 = 0)")
+
+
+def check_closed_form_content(orc):
+    """T = 2, causal, one content dimension, no prior (alpha = inf), Dh = 4.
+
+    q_1 = (2, 0, 0, 0), k_0 = (0, ...), k_1 = (1, 0, 0, 0): scaled scores 0 and 2 / sqrt(4) = 1.
+    Weight of key 1 = 1 / (1 + e^-1); lse_1 = ln(1 + e).
+    """
+    q = np.zeros((1, 1, 2, 4))
+    k = np.zeros((1, 1, 2, 4))
+    v = np.zeros((1, 1, 2, 4))
+    q[0, 0, 1, 0] = 2.0
+    k[0, 0, 1, 0] = 1.0
+    v[0, 0, 1, 2] = 1.0
+    O, lse = orc.attn_fwd(q, k, v, np.array([np.inf]), np.array([0.7]), np.zeros(1), np.ones(1),
+                          causal=True, ssmax=False)
+    _close(O[0, 0, 1], [0.0, 0.0, 1.0 / (1.0 + math.exp(-1.0)), 0.0], 1e-15, "content closed form")
+    _close(lse[0, 0, 1], math.log(1.0 + math.e), 1e-15, "content closed form lse")
+
+
+# ----------------------------------------------------------------------------------
+# reductions to torch SDPA (fp64, CPU)
+# ----------------------------------------------------------------------------------
+
+def _sdpa_reference(q, k, v, mask_fn, c_fn, causal):
+    """softmax(c_i q.k / sqrt(Dh) + c_i * mask(i, j)) V via torch's SDPA, fp64."""
+    import torch
+    B, H, T, Dh = q.shape
+    out = np.empty_like(q)
+    i = torch.arange(T, dtype=torch.float64)[:, None]
+    j = torch.arange(T, dtype=torch.float64)[None, :]
+    for h in range(H):
+        c = c_fn(h, T)                      # [T] tensor
+        mask = c[:, None] * mask_fn(h, i, j)
+        if causal:
+            mask = torch.where(j <= i, mask, torch.tensor(-math.inf, dtype=torch.float64))
+        qq = torch.from_numpy(np.ascontiguousarray(q[:, h])) * c[None, :, None]
+        kk = torch.from_numpy(np.ascontiguousarray(k[:, h]))
+        vv = torch.from_numpy(np.ascontiguousarray(v[:, h]))
+        o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask)
+        out[:, h] = o.numpy()
+    return out
+
+
+def _c_fn(s, ssmax, causal):
+    import torch
+
+    def f(h, T):
+        n = torch.arange(1, T + 1, dtype=torch.float64) if causal else torch.full((T,), float(T), dtype=torch.float64)
+        return s[h] * torch.log(n) if ssmax else torch.ones(T, dtype=torch.float64)
+    return f
+
+
+def _rand_qkv(seed, B=2, H=3, T=37, Dh=8):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, T, Dh)), rng.standard_normal((B, H, T, Dh)),
+            rng.standard_normal((B, H, T, Dh)))
+
+
+def check_alibi_reduction(orc):
+    """beta = 1, mu = 0, alpha = 1/m_h  ==  scores - m_h |i - j| (no pow anywhere)."""
+    import torch
+    q, k, v = _rand_qkv(11, H=12)
+    H = q.shape[1]
+    m = alibi_slopes(H)
+    s = np.linspace(0.3, 0.6, H)
+    for causal in (True, False):
+        for ssmax in (False, True):
+            O, _ = orc.attn_fwd(q, k, v, 1.0 / m, np.ones(H), np.zeros(H), s, causal=causal, ssmax=ssmax)
+            ref = _sdpa_reference(q, k, v, lambda h, i, j: -m[h] * torch.abs(i - j),
+                                  _c_fn(s, ssmax, causal), causal)
+            _close(O, ref, 1e-12, f"ALiBi reduction causal={causal} ssmax={ssmax}")
+
+
+def check_nope_reduction(orc):
+    """alpha = inf (uniform prior) and beta = 0 (constant bias) both equal plain attention."""
+    q, k, v = _rand_qkv(12)
+    H = q.shape[1]
+    s = np.array([0.3, 0.45, 0.6])
+    for causal in (True, False):
+        for ssmax in (False, True):
+            ref = _sdpa_reference(q, k, v, lambda h, i, j: 0.0 * i * j, _c_fn(s, ssmax, causal), causal)
+            O, _ = orc.attn_fwd(q, k, v, np.full(H, np.inf), np.array([0.5, 1.0, 2.0]), np.zeros(H), s,
+                                causal=causal, ssmax=ssmax)
+            _close(O, ref, 1e-12, f"NoPE (alpha=inf) causal={causal} ssmax={ssmax}")
+            O, _ = orc.attn_fwd(q, k, v, np.array([1.0, 7.0, 100.0]), np.zeros(H), np.zeros(H), s,
+                                causal=causal, ssmax=ssmax)
+            _close(O, ref, 1e-12, f"NoPE (beta=0) causal={causal} ssmax={ssmax}")
+
+
+def check_gaussian_reduction(orc):
+    """beta = 2: bias = -((i - j - mu) / alpha)^2, built by multiplication; mu != 0 pins the offset sign."""
+    q, k, v = _rand_qkv(13)
+    H = q.shape[1]
+    alpha = np.array([1.5, 4.0, 20.0])
+    mu = np.array([0.0, -0.5, 0.7])
+    s = np.array([0.35, 0.5, 0.55])
+
+    def mask(h, i, j):
+        x = (i - j - mu[h]) / alpha[h]
+        return -(x * x)
+    for causal in (True, False):
+        for ssmax in (False, True):
+            O, _ = orc.attn_fwd(q, k, v, alpha, np.full(H, 2.0), mu, s, causal=causal, ssmax=ssmax)
+            ref = _sdpa_reference(q, k, v, mask, _c_fn(s, ssmax, causal), causal)
+            _close(O, ref, 1e-12, f"Gaussian reduction causal={causal} ssmax={ssmax}")
+
+
+def check_sqrt_reductions(orc):
+    """beta = 1/2: bias = -sqrt(|x| / alpha); beta = -1/2 (inverted prior): bias = -rsqrt(|x| / alpha)."""
+    import torch
+    q, k, v = _rand_qkv(14)
+    H = q.shape[1]
+    alpha = np.array([0.7, 3.0, 30.0])
+    s = np.array([0.4, 0.45, 0.5])
+    for beta, mu in ((0.5, np.zeros(H)), (-0.5, np.full(H, -0.5))):
+        def mask(h, i, j, beta=beta, mu=mu):
+            u = torch.abs(i - j - mu[h]) / alpha[h]
+            return -torch.sqrt(u) if beta > 0 else -torch.rsqrt(u)
+        for causal in (True, False):
+            for ssmax in (False, True):
+                O, _ = orc.attn_fwd(q, k, v, alpha, np.full(H, beta), mu, s, causal=causal, ssmax=ssmax)
+                ref = _sdpa_reference(q, k, v, mask, _c_fn(s, ssmax, causal), causal)
+                _close(O, ref, 1e-12, f"beta={beta} reduction causal={causal} ssmax={ssmax}")
+
+
+# ----------------------------------------------------------------------------------
+# brute force (mpmath, explicit loops, no max subtraction)
+# ----------------------------------------------------------------------------------
+
+def _brute_row(qi, K, V, i, keys, alpha, beta, mu, s, ssmax, n):
+    import mpmath as mp
+    Dh = len(qi)
+    c = mp.mpf(s) * mp.log(n) if ssmax else mp.mpf(1)
+    logits = []
+    for j in keys:
+        dot = mp.fsum(mp.mpf(qi[e]) * mp.mpf(K[j][e]) for e in range(Dh))
+        x = mp.mpf(i - j) - mp.mpf(mu)
+        u = abs(x) / mp.mpf(alpha)
+        if beta == 0:
+            b = mp.mpf(-1)
+        elif u == 0:
+            b = mp.mpf(0)
+        else:
+            b = -mp.exp(mp.mpf(beta) * mp.log(u))
+        logits.append(c * (dot / mp.sqrt(Dh) + b))
+    w = [mp.exp(t) for t in logits]
+    Z = mp.fsum(w)
+    o = [mp.fsum(w[a] * mp.mpf(V[j][e]) for a, j in enumerate(keys)) / Z for e in range(len(V[0]))]
+    return [float(x) for x in o], float(mp.log(Z))
+
+
+def check_brute_force(orc):
+    import mpmath as mp
+    mp.mp.dps = 40
+    rng = np.random.default_rng(15)
+    B, H, T, Dh = 1, 3, 6, 4
+    q = rng.standard_normal((B, H, T, Dh))
+    k = rng.standard_normal((B, H, T, Dh))
+    v = rng.standard_normal((B, H, T, Dh))
+    alpha = np.array([0.8, 2.5, 9.0])
+    beta = np.array([0.35, 1.3, -0.6])
+    mu = np.array([0.0, 0.3, -0.5])
+    s = np.array([0.4, 0.6, 0.5])
+    for causal in (True, False):
+        for ssmax in (False, True):
+            O, lse = orc.attn_fwd(q, k, v, alpha, beta, mu, s, causal=causal, ssmax=ssmax)
+            for h in range(H):
+                for i in range(T):
+                    keys = list(range(i + 1)) if causal else list(range(T))
+                    o, l = _brute_row(q[0, h, i], k[0, h], v[0, h], i, keys, alpha[h], beta[h], mu[h],
+                                      s[h], ssmax, len(keys))
+                    _close(O[0, h, i], o, 1e-13, f"brute force O h={h} i={i} causal={causal} ssmax={ssmax}")
+                    _close(lse[0, h, i], l, 1e-13, f"brute force lse h={h} i={i} causal={causal} ssmax={ssmax}")
+
+
+# ----------------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------------
+
+def check_invariants(orc):
+    rng = np.random.default_rng(16)
+    T, Dh = 9, 9
+    q = rng.standard_normal((1, 1, T, Dh))
+    k = rng.standard_normal((1, 1, T, Dh))
+    a, b, mu, s = np.array([3.0]), np.array([0.6]), np.array([0.0]), np.array([0.5])
+    for causal in (True, False):
+        eye = np.eye(T)[None, None]
+        P, _ = orc.attn_fwd(q, k, eye, a, b, mu, s, causal=causal, ssmax=True)
+        _close(P[0, 0].sum(axis=1), np.ones(T), 1e-14, "rows of P sum to 1")
+        assert np.all(P >= 0), "P is non-negative"
+        if causal:
+            _close(np.triu(P[0, 0], 1), np.zeros((T, T)), 0.0, "causal: no weight on future keys")
+        Pd = orc.attention_probs(q[0, 0], k[0, 0], a[0], b[0], mu[0], s[0], causal=causal, ssmax=True)
+        _close(P[0, 0], Pd, 1e-15, "V = I returns P")
+        ones = np.ones((1, 1, T, 4))
+        O1, _ = orc.attn_fwd(q, k, ones, a, b, mu, s, causal=causal, ssmax=True)
+        _close(O1, ones, 1e-14, "V = 1 returns 1")
+    v = rng.standard_normal((1, 1, T, 5))
+    O, lse = orc.attn_fwd(q, k, v, a, b, mu, s, causal=True, ssmax=False)
+    _close(O[0, 0, 0], v[0, 0, 0], 1e-15, "first causal row copies V_0")
+    _close(lse[0, 0, 0], q[0, 0, 0] @ k[0, 0, 0] / 3.0, 1e-14, "first causal row lse = q0.k0/sqrt(Dh) + b(0)")
+
+
+def check_weight_ratio_law(orc):
+    """ALiBi, equal content: P[i, j1] / P[i, j2] = exp(-m (d1 - d2))."""
+    H, T = 4, 11
+    m = alibi_slopes(H)
+    q = np.zeros((T, 2))
+    k = np.zeros((T, 2))
+    for h in range(H):
+        P = orc.attention_probs(q, k, 1.0 / m[h], 1.0, 0.0, 1.0, causal=True, ssmax=False)
+        i = T - 1
+        for j1 in range(i):
+            d1, d2 = i - j1, i - (j1 + 1)
+            _close(P[i, j1] / P[i, j1 + 1], math.exp(-m[h] * (d1 - d2)), 1e-13, "weight-ratio law")
+
+
+def check_decode(orc):
+    """Decode of the last token equals the last prefill row and the brute force."""
+    import mpmath as mp
+    mp.mp.dps = 40
+    rng = np.random.default_rng(17)
+    B, H, L, Dh = 2, 3, 7, 4
+    kc = rng.standard_normal((B, H, L, Dh))
+    vc = rng.standard_normal((B, H, L, Dh))
+    qd = rng.standard_normal((B, H, Dh))
+    kv_len = np.array([7, 4])
+    alpha = np.array([0.9, 3.0, 2.0])
+    beta = np.array([0.5, 1.0, -0.4])
+    mu = np.array([0.0, 0.0, -0.5])
+    s = np.array([0.45, 0.45, 0.45])
+    O, lse = orc.attn_decode(qd, kc, vc, kv_len, alpha, beta, mu, s, ssmax=True)
+    for b in range(B):
+        n = int(kv_len[b])
+        q = np.zeros((1, H, n, Dh))
+        q[0, :, n - 1] = qd[b]
+        Of, lf = orc.attn_fwd(q, kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], alpha, beta, mu, s, causal=True, ssmax=True)
+        _close(O[b], Of[0, :, n - 1], 1e-14, "decode = last prefill row")
+        _close(lse[b], lf[0, :, n - 1], 1e-14, "decode lse = last prefill row")
+        for h in range(H):
+            o, l = _brute_row(qd[b, h], kc[b, h], vc[b, h], n - 1, list(range(n)), alpha[h], beta[h], mu[h],
+                              s[h], True, n)
+            _close(O[b, h], o, 1e-13, "decode brute force")
+            _close(lse[b, h], l, 1e-13, "decode brute force lse")
+
+
+# ----------------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------------
+
+def _loss(orc, q, k, v, do, alpha, beta, mu, s, causal, ssmax):
+    O, _ = orc.attn_fwd(q, k, v, alpha, beta, mu, s, causal=causal, ssmax=ssmax)
+    return float((O * do).sum())
+
+
+def check_backward_fd(orc):
+    rng = np.random.default_rng(18)
+    B, H, T, Dh = 1, 3, 6, 4
+    q = rng.standard_normal((B, H, T, Dh))
+    k = rng.standard_normal((B, H, T, Dh))
+    v = rng.standard_normal((B, H, T, Dh))
+    do = rng.standard_normal((B, H, T, Dh))
+    alpha = np.array([0.8, 2.5, 3.0])
+    beta = np.array([0.45, 1.3, -0.6])
+    mu = np.array([0.0, 0.0, -0.5])
+    s = np.array([0.4, 0.6, 0.5])
+    eps = 1e-6
+    for causal in (True, False):
+        for ssmax in (True, False):
+            g = orc.attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=causal, ssmax=ssmax)
+            args = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, s=s)
+            keys = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "s": "ds"}
+            for name, gname in keys.items():
+                x = args[name]
+                num = np.zeros_like(x)
+                for idx in np.ndindex(x.shape):
+                    xp = x.copy()
+                    xm = x.copy()
+                    xp[idx] += eps
+                    xm[idx] -= eps
+                    ap = dict(args, **{name: xp})
+                    am = dict(args, **{name: xm})
+                    fp = _loss(orc, ap["q"], ap["k"], ap["v"], do, ap["alpha"], ap["beta"], mu, ap["s"], causal, ssmax)
+                    fm = _loss(orc, am["q"], am["k"], am["v"], do, am["alpha"], am["beta"], mu, am["s"], causal, ssmax)
+                    num[idx] = (fp - fm) / (2 * eps)
+                if name == "s" and not ssmax:
+                    num[...] = 0.0
+                scale = max(1.0, np.max(np.abs(num)))
+                _close(g[gname], num, 2e-7 * scale, f"backward FD {gname} causal={causal} ssmax={ssmax}")
+
+
+def check_dalpha_alibi_closed_form(orc):
+    """beta = 1, alpha = 1/m: db/dalpha = |d| / alpha^2 = m^2 |d|; db/dbeta = -m|d| ln(m|d|)."""
+    d = np.arange(0, 50)
+    for m in (0.25, 1.0 / 16, 1.0 / 256):
+        _close(orc.prior_bias_dalpha(d, 1.0 / m, 1.0, 0.0), m * m * np.abs(d), 1e-15, "ALiBi db/dalpha")
+        u = m * d[1:]
+        _close(orc.prior_bias_dbeta(d[1:], 1.0 / m, 1.0, 0.0), -u * np.log(u), 1e-15, "ALiBi db/dbeta")
+        _close(orc.prior_bias(d, 1.0 / m, 1.0, 0.0), -m * np.abs(d), 1e-15, "ALiBi bias")
+
+
+def check_special_values(orc):
+    d = np.arange(-4, 5)
+    _close(orc.prior_bias(d, 3.0, 0.0, 0.0), -np.ones(d.size), 0.0, "beta = 0 gives -1 (0^0 = 1)")
+    _close(orc.prior_bias(d, np.inf, 0.7, 0.0), np.zeros(d.size), 0.0, "alpha = inf gives 0")
+    _close(orc.prior_bias(np.array([0]), 2.0, 0.5, 0.0), [0.0], 0.0, "u = 0 with beta > 0 gives 0")
+    try:
+        orc.prior_bias(np.array([0]), 2.0, -0.5, 0.0)
+    except orc.PreconditionError:
+        pass
+    else:
+        raise AssertionError("u = 0 with beta < 0 must raise")
+
+
+ALL_CHECKS = [
+    check_worked_example, check_closed_form_offset_ssmax, check_closed_form_content,
+    check_alibi_reduction, check_nope_reduction, check_gaussian_reduction, check_sqrt_reductions,
+    check_brute_force, check_invariants, check_weight_ratio_law, check_decode, check_backward_fd,
+    check_dalpha_alibi_closed_form, check_special_values,
+]
