@@ -1,0 +1,161 @@
+/*
+ * bam.h - C ABI of the BAM attention library (libbam.so) for AMD Instinct MI355X (gfx950).
+ *
+ * BAM (Bayesian Attention Mechanism) attention is causal scaled-dot-product attention
+ * whose logits carry a per-head Generalized-Gaussian positional prior and are then
+ * rescaled by Scalable-Softmax (SSMax):
+ *
+ *   b_h(d)   = -| (d - mu_h) / alpha_h |^beta_h,   d = i - j  (i query, j key)
+ *   logit_ij = c_i * ( q_i . k_j / sqrt(Dh) + b_h(i - j) )
+ *   c_i      = s_h * ln(n_i) with BAM_SSMAX (n_i = keys visible to query i), else 1
+ *   P        = row softmax(logit),  O = P V,  lse_i = ln sum_j exp(logit_ij)
+ *
+ * Sources: "Bayesian Attention Mechanism" (authors' README), section "Implementation
+ * Details" (per-head additive bias from a Generalized Gaussian prior, trained scale and
+ * shape); "Résumé Technique : Mécanisme d'Attention Bayésienne (BAM)", section
+ * "Solution Proposée : GGD-BAM" (the bias formula with alpha, beta, mu; beta in (0,1)
+ * heavy-tailed, beta < 0 inverted; SSMax rescales logits); "ALiBi: Attention with
+ * Linear Biases", section "Code" (scores = Q K^T / sqrt(d_k), add the bias, softmax).
+ * Conventions where the pages are silent: the offset is taken as (i - j) - mu, there is
+ * no epsilon, the SSMax factor is c_i above (the pages give no formula), lse is the
+ * natural log.  Special values: u = |d - mu| / alpha; u = 0 and beta > 0 gives 0;
+ * beta = 0 gives -1; alpha = +inf gives u = 0.  ALiBi (beta = 1, mu = 0,
+ * alpha = 1 / m_h) and NoPE (alpha = +inf) are special cases.
+ *
+ * Memory and ownership
+ *   - Every tensor argument is a DEVICE pointer on the current HIP device, allocated
+ *     and owned by the caller.  The library allocates nothing and keeps no mutable
+ *     global state; calls on different streams may run concurrently.
+ *   - Dense tensors are row-major with the head dimension contiguous:
+ *     q, k, v, o, dout, dq, dk, dv: [B, H, T, Dh];  lse: [B, H, T] float32.
+ *   - alpha, beta, mu, s: float32[H] on the device.  mu may be NULL (all zero).  s is
+ *     read only when BAM_SSMAX is set (it may be NULL otherwise).
+ *   - Element types: BAM_BF16 (bfloat16 bits) or BAM_F32.  Data pointers must be 16-byte
+ *     aligned.
+ *   - workspace: caller-provided device scratch of at least bam_*_workspace_size()
+ *     bytes, 256-byte aligned; its contents on entry do not matter.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  Calls
+ *     return without synchronising; outputs are valid once the stream has reached them.
+ *   - Inputs are never written.  Outputs are fully overwritten (dalpha, dbeta, ds too).
+ *
+ * Errors
+ *   Host-checkable problems are reported before anything is enqueued, with no partial
+ *   writes: BAM_EINVAL (null or misaligned pointer, non-positive size), BAM_EUNSUPPORTED
+ *   (a dtype / head size / flag combination this build has no kernel for), BAM_EWORKSPACE
+ *   (workspace too small).  A failed kernel launch returns BAM_EHIP.  Values that live on
+ *   the device cannot be checked without a synchronisation and are preconditions:
+ *   alpha > 0 (+inf allowed), beta finite, s > 0, 1 <= kv_len[b] <= Lmax, and for
+ *   beta < 0 that d - mu != 0 for every visible distance d (otherwise the bias is -inf
+ *   and that key is dropped).
+ */
+#ifndef BAM_H
+#define BAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int bam_status;
+#define BAM_OK            0
+#define BAM_EINVAL        1
+#define BAM_EUNSUPPORTED  2
+#define BAM_EWORKSPACE    3
+#define BAM_EHIP          4
+
+/* element types */
+#define BAM_BF16 0
+#define BAM_F32  1
+
+/* flags */
+#define BAM_CAUSAL 1u   /* key j visible to query i only when j <= i */
+#define BAM_SSMAX  2u   /* multiply the logits of query i by c_i = s_h ln(n_i) */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* bam_status_string(bam_status status);
+
+/* Library ABI version (major * 100 + minor). */
+int bam_version(void);
+
+/*
+ * bam_prior_table - the per-head distance table of the GGD prior.
+ *
+ * Writes tab[h * n + t] = b_h(d0 + t) for t in [0, n), h in [0, H), in float32, where
+ * b_h is the bias above (computed in float64, rounded once).  With dalpha / dbeta
+ * non-NULL it also writes the parameter derivatives of the bias,
+ *   dalpha[h * n + t] = db/dalpha = beta u^beta / alpha,
+ *   dbeta [h * n + t] = db/dbeta  = -u^beta ln u          (both 0 where u = 0).
+ * The attention entry points build this table themselves; it is exported so the table
+ * can be checked on its own.  Because the bias depends on i - j only, one row of n
+ * entries per head replaces the T x T bias matrix that the pages' module materialises
+ * ("Bayesian Attention Mechanism", "Implementation Details").
+ */
+bam_status bam_prior_table(const float* alpha, const float* beta, const float* mu, int H,
+                           int d0, int n, float* tab, float* dalpha, float* dbeta,
+                           void* stream);
+
+/*
+ * bam_attn_fwd - prefill forward.
+ *
+ * q, k, v: [B, H, T, Dh] of in_dtype.  flags: BAM_CAUSAL and/or BAM_SSMAX.
+ * Without BAM_CAUSAL every query sees all T keys (n_i = T).
+ * o: [B, H, T, Dh] of o_dtype (BAM_BF16 output is the round-to-nearest-even of the
+ * float32 result).  lse: [B, H, T] float32, natural log.
+ * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128} (bf16 MFMA, fp32 accumulate);
+ * in_dtype BAM_F32 with Dh in {32, 64} (fp32 throughout).
+ */
+size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
+bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                        int B, int H, int T, int Dh,
+                        const float* alpha, const float* beta, const float* mu, const float* s,
+                        unsigned flags, void* o, int o_dtype, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bam_attn_decode - one new query row per sequence against a KV cache (split-KV).
+ *
+ * q: [B, H, Dh]; k_cache, v_cache: [B, H, Lmax, Dh] of in_dtype; kv_len: device
+ * int32[B].  The cache already holds the current token, so the query of sequence b sits
+ * at position i = kv_len[b] - 1 and sees keys 0 .. kv_len[b] - 1 (causal is implied;
+ * n = kv_len[b] for SSMax).  o: [B, H, Dh] of o_dtype; lse: [B, H] float32.
+ * flags: BAM_SSMAX only.  Supported: in_dtype BAM_BF16 with Dh in {64, 128}.
+ * The key range is cut into splits processed in parallel and merged exactly by their
+ * log-sum-exp; the result does not depend on the split count beyond float rounding.
+ */
+size_t bam_decode_workspace_size(int B, int H, int Lmax, int Dh);
+bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                           const int32_t* kv_len, int B, int H, int Lmax, int Dh,
+                           const float* alpha, const float* beta, const float* mu, const float* s,
+                           unsigned flags, void* o, int o_dtype, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bam_attn_bwd - backward of bam_attn_fwd for L = sum(O * dout).
+ *
+ * q, k, v, dout: [B, H, T, Dh] of in_dtype; o: the forward output, [B, H, T, Dh] of
+ * o_dtype; lse: the forward's [B, H, T].  Same flags as the forward call.
+ * dq, dk, dv: [B, H, T, Dh] of grad_dtype.  dalpha, dbeta, ds: device float32[H], the
+ * gradients with respect to alpha_h, beta_h and s_h summed over batch, queries and keys
+ * (ds is 0 without BAM_SSMAX).  With dP = dout V^T, D_i = sum_e dout_ie O_ie and
+ * dZ = P * (dP - D) (the gradient with respect to the logits):
+ *   dV = P^T dout,  dQ_i = c_i sum_j dZ_ij k_j / sqrt(Dh),  dK_j = sum_i c_i dZ_ij q_i / sqrt(Dh),
+ *   dalpha = sum c_i dZ_ij db/dalpha,  dbeta = sum c_i dZ_ij db/dbeta,
+ *   ds = sum dZ_ij ln(n_i) (q_i.k_j / sqrt(Dh) + b_ij).
+ * Supported: in_dtype BAM_BF16 with Dh in {32, 64}.
+ */
+size_t bam_bwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
+bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                        const float* lse, const void* dout, int in_dtype,
+                        int B, int H, int T, int Dh,
+                        const float* alpha, const float* beta, const float* mu, const float* s,
+                        unsigned flags, void* dq, void* dk, void* dv, int grad_dtype,
+                        float* dalpha, float* dbeta, float* ds,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BAM_H */

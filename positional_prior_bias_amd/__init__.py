@@ -1,0 +1,256 @@
+"""BAM attention on AMD Instinct MI355X (gfx950): Python binding of libbam.so.
+
+The functions here carry the C entry points' names (include/bam.h) and only
+marshal arguments: they check tensor placement, allocate outputs and the
+workspace with torch, and pass raw device pointers plus torch's current HIP
+stream to the library.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback path.  If libbam.so has not been built the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BamError", "lib", "lib_path",
+    "bam_prior_table", "bam_attn_fwd", "bam_attn_decode", "bam_attn_bwd",
+    "bam_fwd_workspace_size", "bam_decode_workspace_size", "bam_bwd_workspace_size",
+    "EXPORTED_SYMBOLS",
+]
+
+BAM_BF16 = 0
+BAM_F32 = 1
+BAM_CAUSAL = 1
+BAM_SSMAX = 2
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+EXPORTED_SYMBOLS = (
+    "bam_status_string", "bam_version", "bam_prior_table",
+    "bam_fwd_workspace_size", "bam_attn_fwd",
+    "bam_decode_workspace_size", "bam_attn_decode",
+    "bam_bwd_workspace_size", "bam_attn_bwd",
+)
+
+
+class BamError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return os.path.join(_DIR, "libbam.so")
+
+
+def _declare(L):
+    vp, i, u, sz, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t, ctypes.c_void_p
+    L.bam_status_string.restype = ctypes.c_char_p
+    L.bam_status_string.argtypes = [i]
+    L.bam_version.restype = i
+    L.bam_version.argtypes = []
+    L.bam_prior_table.restype = i
+    L.bam_prior_table.argtypes = [fp, fp, fp, i, i, i, fp, fp, fp, vp]
+    L.bam_fwd_workspace_size.restype = sz
+    L.bam_fwd_workspace_size.argtypes = [i, i, i, i, u]
+    L.bam_attn_fwd.restype = i
+    L.bam_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp, sz, vp]
+    L.bam_decode_workspace_size.restype = sz
+    L.bam_decode_workspace_size.argtypes = [i, i, i, i]
+    L.bam_attn_decode.restype = i
+    L.bam_attn_decode.argtypes = [vp, vp, vp, i, vp, i, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp, sz, vp]
+    L.bam_bwd_workspace_size.restype = sz
+    L.bam_bwd_workspace_size.argtypes = [i, i, i, i, u]
+    L.bam_attn_bwd.restype = i
+    L.bam_attn_bwd.argtypes = [vp, vp, vp, vp, i, fp, vp, i, i, i, i, i, fp, fp, fp, fp, u,
+                               vp, vp, vp, i, fp, fp, fp, vp, sz, vp]
+
+
+def lib():
+    """Load libbam.so (once).  Raises BamError if it is missing."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise BamError(f"{path} is not built; run `python -m positional_prior_bias_amd.build`")
+        L = ctypes.CDLL(path)
+        _declare(L)
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise BamError(f"{what}: {lib().bam_status_string(status).decode()} (status {status})")
+
+
+# ---------------------------------------------------------------------------------------
+# torch marshalling helpers
+# ---------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BAM_BF16
+    if t.dtype == torch.float32:
+        return BAM_F32
+    raise BamError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return torch.bfloat16 if code == BAM_BF16 else torch.float32
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise BamError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise BamError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _params(alpha, beta, mu, s, flags):
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        if t is None or t.dtype != _torch().float32:
+            raise BamError(f"{name} must be a float32 device tensor of length H")
+    return _dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), _dev(s, "s") if (flags & BAM_SSMAX) else _ptr(s)
+
+
+def _workspace(nbytes, device, workspace=None):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise BamError("workspace too small")
+        return workspace
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _flags(causal: bool, ssmax: bool) -> int:
+    return (BAM_CAUSAL if causal else 0) | (BAM_SSMAX if ssmax else 0)
+
+
+# ---------------------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------------------
+
+def bam_fwd_workspace_size(B, H, T, Dh, flags) -> int:
+    return int(lib().bam_fwd_workspace_size(B, H, T, Dh, flags))
+
+
+def bam_decode_workspace_size(B, H, Lmax, Dh) -> int:
+    return int(lib().bam_decode_workspace_size(B, H, Lmax, Dh))
+
+
+def bam_bwd_workspace_size(B, H, T, Dh, flags) -> int:
+    return int(lib().bam_bwd_workspace_size(B, H, T, Dh, flags))
+
+
+def bam_prior_table(alpha, beta, mu, d0: int, n: int, derivatives: bool = False, stream=None):
+    """tab[h, t] = b_h(d0 + t) (float32 [H, n]); with derivatives also db/dalpha, db/dbeta."""
+    torch = _torch()
+    H = alpha.numel()
+    tab = torch.empty((H, n), dtype=torch.float32, device=alpha.device)
+    da = torch.empty_like(tab) if derivatives else None
+    db = torch.empty_like(tab) if derivatives else None
+    st = lib().bam_prior_table(_dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), H, d0, n,
+                               _ptr(tab), _ptr(da), _ptr(db), _stream(stream))
+    _check(st, "bam_prior_table")
+    return (tab, da, db) if derivatives else tab
+
+
+def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True, o_dtype=None,
+                 o=None, lse=None, workspace=None, stream=None):
+    """Prefill forward; q, k, v [B, H, T, Dh].  Returns (o, lse)."""
+    torch = _torch()
+    B, H, T, Dh = q.shape
+    flags = _flags(causal, ssmax)
+    in_code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != q.shape or v.shape != q.shape:
+        raise BamError("q, k, v must share shape and dtype")
+    oc = in_code if o_dtype is None else (_dtype_code(torch.empty(0, dtype=o_dtype)))
+    if o is None:
+        o = torch.empty((B, H, T, Dh), dtype=_torch_dtype(oc), device=q.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    nb = bam_fwd_workspace_size(B, H, T, Dh, flags)
+    ws = _workspace(nb, q.device, workspace)
+    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    st = lib().bam_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), in_code, B, H, T, Dh, a, b_, m_, s_,
+                            flags, _dev(o, "o"), oc, _dev(lse, "lse"), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "bam_attn_fwd")
+    return o, lse
+
+
+def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, ssmax=True, o_dtype=None,
+                    o=None, lse=None, workspace=None, stream=None):
+    """Decode; q [B, H, Dh], caches [B, H, Lmax, Dh], kv_len int32 [B].  Returns (o, lse)."""
+    torch = _torch()
+    B, H, Lmax, Dh = k_cache.shape
+    flags = _flags(False, ssmax)
+    in_code = _dtype_code(k_cache)
+    if kv_len.dtype != torch.int32:
+        raise BamError("kv_len must be int32")
+    oc = in_code if o_dtype is None else _dtype_code(torch.empty(0, dtype=o_dtype))
+    if o is None:
+        o = torch.empty((B, H, Dh), dtype=_torch_dtype(oc), device=q.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nb = bam_decode_workspace_size(B, H, Lmax, Dh)
+    ws = _workspace(nb, q.device, workspace)
+    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    st = lib().bam_attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), in_code,
+                               _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
+                               _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "bam_attn_decode")
+    return o, lse
+
+
+def bam_attn_bwd(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
+                 grad_dtype=None, workspace=None, stream=None):
+    """Backward.  Returns (dq, dk, dv, dalpha, dbeta, ds)."""
+    torch = _torch()
+    B, H, T, Dh = q.shape
+    flags = _flags(causal, ssmax)
+    in_code = _dtype_code(q)
+    gc = in_code if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
+    gdt = _torch_dtype(gc)
+    dq = torch.empty_like(q, dtype=gdt)
+    dk = torch.empty_like(q, dtype=gdt)
+    dv = torch.empty_like(q, dtype=gdt)
+    dalpha = torch.empty(H, dtype=torch.float32, device=q.device)
+    dbeta = torch.empty_like(dalpha)
+    ds = torch.empty_like(dalpha)
+    nb = bam_bwd_workspace_size(B, H, T, Dh, flags)
+    ws = _workspace(nb, q.device, workspace)
+    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    st = lib().bam_attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dtype_code(o),
+                            _dev(lse, "lse"), _dev(dout, "dout"), in_code, B, H, T, Dh, a, b_, m_, s_, flags,
+                            _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), gc, _dev(dalpha, "dalpha"),
+                            _dev(dbeta, "dbeta"), _dev(ds, "ds"), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _check(st, "bam_attn_bwd")
+    return dq, dk, dv, dalpha, dbeta, ds

@@ -1,0 +1,270 @@
+// C ABI of libbam.so: argument validation, workspace carving and kernel launches.
+// The declarations, layouts, ownership and error rules are documented in include/bam.h.
+#include <stdint.h>
+
+#include <cmath>
+
+#include "../../include/bam.h"
+#include "bam_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+int pad64(int n) { return (n + 63) / 64 * 64; }
+
+// Distance-table geometry: causal rows need d in [0, T-1]; non-causal [-(T-1), T-1].
+struct TableGeom {
+  int d0;
+  int n;
+  int stride;
+};
+
+TableGeom table_geom(int T, bool causal) {
+  TableGeom g;
+  g.d0 = causal ? 0 : -(T - 1);
+  g.n = causal ? T : 2 * T - 1;
+  g.stride = pad64(g.n);
+  return g;
+}
+
+bool dims_ok(int B, int H, int T) { return B > 0 && H > 0 && T > 0; }
+
+bam_status hip_status(hipError_t e) { return e == hipSuccess ? BAM_OK : BAM_EHIP; }
+
+bool prior_ok(const float* alpha, const float* beta, const float* s, unsigned flags) {
+  if (alpha == nullptr || beta == nullptr) return false;
+  if ((flags & BAM_SSMAX) && s == nullptr) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bam_status_string(bam_status status) {
+  switch (status) {
+    case BAM_OK: return "ok";
+    case BAM_EINVAL: return "invalid argument";
+    case BAM_EUNSUPPORTED: return "unsupported dtype / head size / flags";
+    case BAM_EWORKSPACE: return "workspace too small";
+    case BAM_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int bam_version(void) { return 100; }
+
+bam_status bam_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
+                           int n, float* tab, float* dalpha, float* dbeta, void* stream) {
+  if (alpha == nullptr || beta == nullptr || tab == nullptr || H <= 0 || n <= 0) return BAM_EINVAL;
+  return hip_status(bam::launch_prior_table(alpha, beta, mu, H, d0, n, n, 1.0f, tab, dalpha, dbeta,
+                                            (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------
+size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags) {
+  (void)B;
+  (void)Dh;
+  if (H <= 0 || T <= 0) return 0;
+  const TableGeom g = table_geom(T, (flags & BAM_CAUSAL) != 0);
+  return align_up((size_t)H * g.stride * sizeof(float));
+}
+
+bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtype, int B, int H, int T,
+                        int Dh, const float* alpha, const float* beta, const float* mu, const float* s,
+                        unsigned flags, void* o, int o_dtype, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      lse == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
+    return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX)) != 0) return BAM_EINVAL;
+  if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
+  if (in_dtype == BAM_BF16) {
+    if (Dh != 32 && Dh != 64 && Dh != 128) return BAM_EUNSUPPORTED;
+  } else if (in_dtype == BAM_F32) {
+    if (Dh != 32 && Dh != 64) return BAM_EUNSUPPORTED;
+  } else {
+    return BAM_EUNSUPPORTED;
+  }
+  if ((size_t)B * H * (size_t)T * Dh > ((size_t)1 << 40)) return BAM_EUNSUPPORTED;
+  if (workspace_bytes < bam_fwd_workspace_size(B, H, T, Dh, flags)) return BAM_EWORKSPACE;
+
+  const bool causal = (flags & BAM_CAUSAL) != 0;
+  const TableGeom g = table_geom(T, causal);
+  hipStream_t st = (hipStream_t)stream;
+  float* tab = (float*)workspace;
+  hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr, st);
+  if (e != hipSuccess) return BAM_EHIP;
+  bam::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.tab = tab;
+  a.s = s;
+  a.tab_d0 = g.d0;
+  a.tab_stride = g.stride;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.causal = causal;
+  a.ssmax = (flags & BAM_SSMAX) != 0;
+  a.o = o;
+  a.o_f32 = o_dtype == BAM_F32;
+  a.lse = lse;
+  e = in_dtype == BAM_BF16 ? bam::launch_fwd_bf16(a, Dh, st) : bam::launch_fwd_f32(a, Dh, st);
+  return hip_status(e);
+}
+
+// ---------------------------------------------------------------------------------------
+namespace {
+struct DecodeLayout {
+  size_t tab_off, part_off, total;
+  int tab_stride, nsplit, chunk;
+};
+
+DecodeLayout decode_layout(int B, int H, int Lmax, int Dh) {
+  DecodeLayout d;
+  d.tab_stride = pad64(Lmax);
+  d.chunk = bam::decode_chunk_keys(Lmax, Dh);
+  d.nsplit = (Lmax + d.chunk - 1) / d.chunk;
+  d.tab_off = 0;
+  d.part_off = align_up((size_t)H * d.tab_stride * sizeof(float));
+  d.total = d.part_off + align_up((size_t)B * H * d.nsplit * (Dh + 2) * sizeof(float));
+  return d;
+}
+}  // namespace
+
+size_t bam_decode_workspace_size(int B, int H, int Lmax, int Dh) {
+  if (B <= 0 || H <= 0 || Lmax <= 0 || (Dh != 64 && Dh != 128)) return 0;
+  return decode_layout(B, H, Lmax, Dh).total;
+}
+
+bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                           const int32_t* kv_len, int B, int H, int Lmax, int Dh, const float* alpha,
+                           const float* beta, const float* mu, const float* s, unsigned flags, void* o,
+                           int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!dims_ok(B, H, Lmax) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(o) || lse == nullptr || kv_len == nullptr || workspace == nullptr ||
+      !prior_ok(alpha, beta, s, flags))
+    return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX)) != 0) return BAM_EINVAL;
+  if (in_dtype != BAM_BF16 || (Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
+  if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
+  const DecodeLayout L = decode_layout(B, H, Lmax, Dh);
+  if (workspace_bytes < L.total) return BAM_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  float* tab = (float*)((char*)workspace + L.tab_off);
+  hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, 0, Lmax, L.tab_stride, 1.0f, tab, nullptr, nullptr, st);
+  if (e != hipSuccess) return BAM_EHIP;
+  bam::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.kv_len = kv_len;
+  a.tab = tab;
+  a.s = s;
+  a.tab_stride = L.tab_stride;
+  a.B = B;
+  a.H = H;
+  a.Lmax = Lmax;
+  a.ssmax = (flags & BAM_SSMAX) != 0;
+  a.nsplit = L.nsplit;
+  a.chunk = L.chunk;
+  a.part = (float*)((char*)workspace + L.part_off);
+  a.o = o;
+  a.o_f32 = o_dtype == BAM_F32;
+  a.lse = lse;
+  return hip_status(bam::launch_decode(a, Dh, st));
+}
+
+// ---------------------------------------------------------------------------------------
+namespace {
+struct BwdLayout {
+  size_t tab_off, ta_off, tb_off, D_off, part_off, total;
+  TableGeom g;
+};
+
+BwdLayout bwd_layout(int B, int H, int T, bool causal) {
+  BwdLayout L;
+  L.g = table_geom(T, causal);
+  const size_t tabsz = align_up((size_t)H * L.g.stride * sizeof(float));
+  L.tab_off = 0;
+  L.ta_off = tabsz;
+  L.tb_off = 2 * tabsz;
+  L.D_off = 3 * tabsz;
+  L.part_off = L.D_off + align_up((size_t)B * H * T * sizeof(float));
+  L.total = L.part_off + align_up(bam::bwd_param_partials(B, H, T) * sizeof(float));
+  return L;
+}
+}  // namespace
+
+size_t bam_bwd_workspace_size(int B, int H, int T, int Dh, unsigned flags) {
+  (void)Dh;
+  if (!dims_ok(B, H, T)) return 0;
+  return bwd_layout(B, H, T, (flags & BAM_CAUSAL) != 0).total;
+}
+
+bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                        const float* lse, const void* dout, int in_dtype, int B, int H, int T, int Dh,
+                        const float* alpha, const float* beta, const float* mu, const float* s,
+                        unsigned flags, void* dq, void* dk, void* dv, int grad_dtype, float* dalpha,
+                        float* dbeta, float* ds, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || lse == nullptr ||
+      dalpha == nullptr || dbeta == nullptr || ds == nullptr || workspace == nullptr ||
+      !prior_ok(alpha, beta, s, flags))
+    return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX)) != 0) return BAM_EINVAL;
+  if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64)) return BAM_EUNSUPPORTED;
+  if ((o_dtype != BAM_BF16 && o_dtype != BAM_F32) || (grad_dtype != BAM_BF16 && grad_dtype != BAM_F32))
+    return BAM_EUNSUPPORTED;
+  const bool causal = (flags & BAM_CAUSAL) != 0;
+  const BwdLayout L = bwd_layout(B, H, T, causal);
+  if (workspace_bytes < L.total) return BAM_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* tab = (float*)(ws + L.tab_off);
+  float* ta = (float*)(ws + L.ta_off);
+  float* tb = (float*)(ws + L.tb_off);
+  hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, L.g.d0, L.g.n, L.g.stride, 1.0f, tab, ta, tb, st);
+  if (e != hipSuccess) return BAM_EHIP;
+  bam::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.o_f32 = o_dtype == BAM_F32;
+  a.lse = lse;
+  a.dout = dout;
+  a.tab = tab;
+  a.tab_da = ta;
+  a.tab_db = tb;
+  a.s = s;
+  a.tab_d0 = L.g.d0;
+  a.tab_stride = L.g.stride;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.causal = causal;
+  a.ssmax = (flags & BAM_SSMAX) != 0;
+  a.Dbuf = (float*)(ws + L.D_off);
+  a.dq_acc = nullptr;
+  a.param_part = (float*)(ws + L.part_off);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.grad_f32 = grad_dtype == BAM_F32;
+  a.dalpha = dalpha;
+  a.dbeta = dbeta;
+  a.ds = ds;
+  return hip_status(bam::launch_bwd(a, Dh, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Host-side declarations shared between the C-ABI module and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bam {
+
+// Launch the distance-table kernel: tab[h*stride + t] = b_h(d0 + t) (and derivatives).
+hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
+                              int n, int stride, float scale, float* tab, float* dalpha, float* dbeta,
+                              hipStream_t stream);
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* tab;   // [H][tab_stride] natural-unit bias, index = d - tab_d0
+  const float* s;     // SSMax strength per head (NULL without SSMax)
+  int tab_d0;         // distance held at index 0
+  int tab_stride;     // floats per head row
+  int B, H, T;
+  bool causal, ssmax;
+  void* o;
+  bool o_f32;
+  float* lse;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int Dh, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, int Dh, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;        // [B,H,Dh]
+  const void* k;        // [B,H,Lmax,Dh]
+  const void* v;
+  const int32_t* kv_len;
+  const float* tab;     // [H][tab_stride], index = d (0 .. Lmax-1)
+  const float* s;
+  int tab_stride;
+  int B, H, Lmax;
+  bool ssmax;
+  int nsplit;           // number of key ranges
+  int chunk;            // keys per range (multiple of the per-block tile)
+  float* part;          // [B,H,nsplit,Dh+2] partial (m, l, o)
+  void* o;
+  bool o_f32;
+  float* lse;
+};
+
+int decode_chunk_keys(int Lmax, int Dh);
+hipError_t launch_decode(const DecodeArgs& a, int Dh, hipStream_t stream);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  bool o_f32;
+  const float* lse;
+  const void* dout;
+  const float* tab;      // bias b(d), index d (causal: 0..T-1; else d + T - 1)
+  const float* tab_da;   // db/dalpha
+  const float* tab_db;   // db/dbeta
+  const float* s;
+  int tab_d0;
+  int tab_stride;
+  int B, H, T;
+  bool causal, ssmax;
+  float* Dbuf;           // [B,H,T] rowsum(dO * O)
+  float* dq_acc;         // [B,H,T,Dh] fp32 accumulator
+  float* param_part;     // [nparts][3][H] per-block partial sums (or direct)
+  void* dq;
+  void* dk;
+  void* dv;
+  bool grad_f32;
+  float* dalpha;
+  float* dbeta;
+  float* ds;
+};
+
+size_t bwd_param_partials(int B, int H, int T);
+hipError_t launch_bwd(const BwdArgs& a, int Dh, hipStream_t stream);
+
+}  // namespace bam

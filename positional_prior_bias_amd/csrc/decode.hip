@@ -1,0 +1,231 @@
+// BAM attention decode: one query row per (b, h) against a long KV cache, split-KV.
+//
+// The query of sequence b sits at position i = kv_len[b] - 1 and sees n = kv_len[b]
+// keys; logit_j = c (q.k_j / sqrt(Dh) + b_h(i - j)), c = s_h ln(n) with SSMax
+// ("Résumé Technique : Mécanisme d'Attention Bayésienne (BAM)", "Solution Proposée :
+// GGD-BAM"; retrieval far beyond the training context, "Bayesian Attention
+// Mechanism", "Highlights").
+//
+// HBM-bound streaming design:
+//   * grid = (nsplit, H, B); a work-group of 4 waves owns one contiguous key range of
+//     one (b, h) and each wave takes every fourth tile of it;
+//   * a tile is 8 fully coalesced 1 KiB loads of K and of V per wave (16-byte loads,
+//     lane l reads bytes 16 l .. 16 l + 15 of each KiB); Dh / 8 lanes share a key, each
+//     holding 8 of its head-dimension entries;
+//   * q.k is a per-lane 8-term dot plus a butterfly over the lanes of a key; the
+//     online softmax keeps (m, l, o) per lane with a wave-uniform running max;
+//   * the partial (m, l, o) of each range goes to the workspace and a second kernel
+//     merges the ranges exactly by their log-sum-exp.
+// The bias of distance d comes from the per-head table (one float per key, read
+// through L2, shared by every sequence of the batch).
+#include <float.h>
+
+#include "bam_device.h"
+#include "bam_internal.h"
+
+namespace bam {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRows = 8;  // 1 KiB loads per tile per tensor
+
+template <int DH>
+struct DecodeShape {
+  static constexpr int LPK = DH / 8;        // lanes per key
+  static constexpr int KPI = 64 / LPK;      // keys per 1 KiB load
+  static constexpr int KT = kRows * KPI;    // keys per wave tile
+};
+
+__device__ __forceinline__ float dot8(const float* q, const u32x4& w) {
+  float acc = q[0] * bf16_lo(w[0]);
+  acc = fmaf(q[1], bf16_hi(w[0]), acc);
+  acc = fmaf(q[2], bf16_lo(w[1]), acc);
+  acc = fmaf(q[3], bf16_hi(w[1]), acc);
+  acc = fmaf(q[4], bf16_lo(w[2]), acc);
+  acc = fmaf(q[5], bf16_hi(w[2]), acc);
+  acc = fmaf(q[6], bf16_lo(w[3]), acc);
+  acc = fmaf(q[7], bf16_hi(w[3]), acc);
+  return acc;
+}
+
+template <int DH>
+__global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
+  using S = DecodeShape<DH>;
+  constexpr int LPK = S::LPK, KPI = S::KPI, KT = S::KT;
+  __shared__ float red[kWaves][DH + 2];
+
+  const int sidx = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int bh = b * a.H + h;
+  int L = a.kv_len[b];
+  L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);   // keep reads in bounds whatever the input
+  const int iq = L - 1;
+  const int kbeg = sidx * a.chunk;
+  const int kend = min(kbeg + a.chunk, L);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int slot = lane / LPK;      // key slot inside a 1 KiB load
+  const int cl = lane % LPK;        // which 8 head-dim entries this lane holds
+
+  const float qscale = kLog2e / __builtin_sqrtf((float)DH);
+  float qv[8];
+  {
+    const u32x4 w = *(const u32x4*)((const uint16_t*)a.q + (size_t)bh * DH + cl * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(w[e]) * qscale;
+      qv[2 * e + 1] = bf16_hi(w[e]) * qscale;
+    }
+  }
+  const float c = ssmax_c(a.ssmax, a.ssmax ? a.s[h] : 1.0f, L);
+  const float C = fmaxf(c, FLT_MIN);
+  const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
+  const size_t kvbase = (size_t)bh * a.Lmax * DH;
+  const uint16_t* __restrict__ Kc = (const uint16_t*)a.k + kvbase;
+  const uint16_t* __restrict__ Vc = (const uint16_t*)a.v + kvbase;
+
+  float m = kNegInf, l = 0.f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+  for (int tb = kbeg + wave * KT; tb < kend; tb += kWaves * KT) {
+    u32x4 kw[kRows], vw[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int key = tb + r * KPI + slot;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kw[r] = z;
+      vw[r] = z;
+      if (key < kend) {
+        kw[r] = __builtin_nontemporal_load((const u32x4*)(Kc + (size_t)key * DH + cl * 8));
+        vw[r] = __builtin_nontemporal_load((const u32x4*)(Vc + (size_t)key * DH + cl * 8));
+      }
+    }
+    float lg[kRows];
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      float d = dot8(qv, kw[r]);
+#pragma unroll
+      for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off, 64);
+      const int key = tb + r * KPI + slot;
+      float t = kNegInf;
+      if (key < kend) t = C * fmaf(tabh[iq - key], kLog2e, d);
+      lg[r] = t;
+      mx = fmaxf(mx, t);
+    }
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float sc = exp2_fast(m - m_use);
+    m = m_new;
+    l *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= sc;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const float p = exp2_fast(lg[r] - m_use);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = fmaf(p, bf16_lo(vw[r][e]), o[2 * e]);
+        o[2 * e + 1] = fmaf(p, bf16_hi(vw[r][e]), o[2 * e + 1]);
+      }
+    }
+  }
+  // sum over the key slots of the wave (same running max everywhere in the wave)
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off, 64);
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][cl * 8 + e] = o[e];
+    if (lane == 0) {
+      red[wave][DH] = m;
+      red[wave][DH + 1] = l;
+    }
+  }
+  __syncthreads();
+  if (tid < DH) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[w][DH]);
+    float Ls = 0.f, Os = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red[w][DH];
+      const float wt = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+      Ls += wt * red[w][DH + 1];
+      Os += wt * red[w][tid];
+    }
+    float* part = a.part + ((size_t)bh * a.nsplit + sidx) * (DH + 2);
+    part[2 + tid] = Os;
+    if (tid == 0) {
+      part[0] = M;
+      part[1] = Ls;
+    }
+  }
+}
+
+template <int DH>
+__global__ void __launch_bounds__(DH) decode_combine_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int e = threadIdx.x;
+  const float* part = a.part + (size_t)bh * a.nsplit * (DH + 2);
+  float M = kNegInf;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[(size_t)s * (DH + 2)]);
+  float Ls = 0.f, Os = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float* ps = part + (size_t)s * (DH + 2);
+    const float ms = ps[0];
+    if (ms == kNegInf) continue;
+    const float wt = exp2_fast(ms - M);
+    Ls += wt * ps[1];
+    Os += wt * ps[2 + e];
+  }
+  const float out = Os / Ls;
+  if (a.o_f32) {
+    ((float*)a.o)[(size_t)bh * DH + e] = out;
+  } else {
+    ((__bf16*)a.o)[(size_t)bh * DH + e] = (__bf16)out;
+  }
+  if (e == 0) a.lse[bh] = (M + __log2f(Ls)) * kLn2;
+}
+
+template <int DH>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_split_kernel<DH>, dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3(a.B * a.H), dim3(DH), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Keys per split: a whole number of work-group tiles, about 2K keys for long caches.
+int decode_chunk_keys(int Lmax, int Dh) {
+  const int tile = kWaves * kRows * (64 / (Dh / 8));
+  int want = 2048;
+  if (Lmax < want) want = Lmax;
+  return ((want + tile - 1) / tile) * tile;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int Dh, hipStream_t stream) {
+  switch (Dh) {
+    case 64: return launch_t<64>(a, stream);
+    case 128: return launch_t<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bam

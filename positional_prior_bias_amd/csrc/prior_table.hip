@@ -1,0 +1,56 @@
+// Per-head distance table of the Generalized-Gaussian positional prior.
+//
+// "Résumé Technique : Mécanisme d'Attention Bayésienne (BAM)", "Solution Proposée :
+// GGD-BAM": b = -|x / alpha|^beta per head.  The offset convention is x = d - mu with
+// d = i - j (query minus key).  The bias depends on the distance only, so one row of
+// n values per head replaces the dense T x T matrix; it is rebuilt on every call since
+// alpha and beta are trained parameters ("Bayesian Attention Mechanism",
+// "Implementation Details").  One pow per (head, distance), evaluated in float64 and
+// rounded once to float32.
+#include "bam_device.h"
+#include "bam_internal.h"
+
+namespace bam {
+
+__global__ void __launch_bounds__(256) prior_table_kernel(const float* __restrict__ alpha,
+                                                          const float* __restrict__ beta,
+                                                          const float* __restrict__ mu, int d0, int n,
+                                                          int stride, float scale, float* __restrict__ tab,
+                                                          float* __restrict__ ta,
+                                                          float* __restrict__ tb) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  if (t >= n) return;
+  const double a = alpha[h];
+  const double be = beta[h];
+  const double m = mu ? (double)mu[h] : 0.0;
+  const double x = (double)(d0 + t) - m;
+  const double u = __builtin_isinf(a) ? 0.0 : fabs(x) / a;
+  double b, da = 0.0, db = 0.0;
+  if (be == 0.0) {
+    b = -1.0;                                   // 0^0 = 1
+    if (u != 0.0) db = -log(u);
+  } else if (u == 0.0) {
+    b = be > 0.0 ? 0.0 : -__builtin_huge_val();  // beta < 0 at u = 0: precondition violated
+  } else {
+    const double p = pow(u, be);
+    b = -p;
+    da = be * p / a;
+    db = -p * log(u);
+  }
+  const size_t idx = (size_t)h * stride + t;
+  tab[idx] = (float)(b * scale);
+  if (ta) ta[idx] = (float)da;
+  if (tb) tb[idx] = (float)db;
+}
+
+hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
+                              int n, int stride, float scale, float* tab, float* dalpha, float* dbeta,
+                              hipStream_t stream) {
+  dim3 grid((n + 255) / 256, H);
+  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), 0, stream, alpha, beta, mu, d0, n, stride, scale,
+                     tab, dalpha, dbeta);
+  return hipGetLastError();
+}
+
+}  // namespace bam

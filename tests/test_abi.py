@@ -1,0 +1,93 @@
+"""C-ABI library: it loads, exports every symbol include/bam.h declares, and the host-side
+argument checks reject bad calls before anything touches the GPU.  No compute calls."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import positional_prior_bias_amd as bam
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bam.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bam_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bam.lib_path()):
+        pytest.fail("libbam.so is not built (run __graft_entry__.build())")
+    return bam.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("bam_attn_fwd", "bam_attn_decode", "bam_attn_bwd", "bam_prior_table"):
+        assert n in names
+    assert set(names) == set(bam.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(bam.lib_path())
+    for n in declared_functions():
+        assert hasattr(raw, n), f"libbam.so does not export {n}"
+
+
+def test_status_strings(L):
+    assert L.bam_status_string(0) == b"ok"
+    assert L.bam_status_string(3) == b"workspace too small"
+    assert L.bam_version() >= 100
+
+
+def test_workspace_sizes(L):
+    # distance table only: H rows of T (causal) or 2T-1 entries padded to 64, 256-byte aligned
+    assert L.bam_fwd_workspace_size(32, 12, 512, 64, 3) == 12 * 512 * 4
+    assert L.bam_fwd_workspace_size(1, 4, 256, 32, 0) == 4 * 512 * 4
+    assert L.bam_fwd_workspace_size(1, 0, 256, 32, 1) == 0
+    assert L.bam_decode_workspace_size(8, 12, 256000, 64) > 12 * 256000 * 4
+    assert L.bam_decode_workspace_size(8, 12, 256000, 48) == 0
+    assert L.bam_bwd_workspace_size(32, 12, 512, 64, 3) >= 3 * 12 * 512 * 4 + 32 * 12 * 512 * 4
+
+
+def _fwd(L, **kw):
+    a = dict(q=16, k=16, v=16, in_dtype=0, B=1, H=1, T=8, Dh=64, alpha=16, beta=16, mu=None, s=16,
+             flags=3, o=16, o_dtype=1, lse=16, ws=256, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return L.bam_attn_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["B"], a["H"], a["T"], a["Dh"],
+                          a["alpha"], a["beta"], a["mu"], a["s"], a["flags"], a["o"], a["o_dtype"],
+                          a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fwd_rejects_bad_arguments_before_launch(L):
+    # pointers here are fake (never dereferenced): every call must fail host-side
+    assert _fwd(L, q=None) == 1
+    assert _fwd(L, q=8) == 1                      # misaligned
+    assert _fwd(L, T=0) == 1
+    assert _fwd(L, flags=4) == 1
+    assert _fwd(L, s=None) == 1                   # SSMax without s
+    assert _fwd(L, Dh=48) == 2
+    assert _fwd(L, in_dtype=7) == 2
+    assert _fwd(L, in_dtype=1, Dh=128) == 2
+    assert _fwd(L, o_dtype=5) == 2
+    assert _fwd(L, wsb=16) == 3
+
+
+def test_decode_and_bwd_reject_bad_arguments(L):
+    st = L.bam_attn_decode(16, 16, 16, 0, None, 1, 1, 8, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None)
+    assert st == 1                                 # kv_len NULL
+    st = L.bam_attn_decode(16, 16, 16, 1, 16, 1, 1, 8, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None)
+    assert st == 2                                 # fp32 caches unsupported
+    st = L.bam_attn_decode(16, 16, 16, 0, 16, 8, 12, 256000, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1024, None)
+    assert st == 3
+    st = L.bam_attn_bwd(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 128, 16, 16, None, 16, 3, 16, 16, 16, 0,
+                        16, 16, 16, 256, 1 << 20, None)
+    assert st == 2                                 # Dh = 128 backward unsupported
+    st = L.bam_attn_bwd(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 64, 16, 16, None, 16, 3, 16, 16, 16, 0,
+                        None, 16, 16, 256, 1 << 20, None)
+    assert st == 1                                 # dalpha NULL
+    assert L.bam_prior_table(None, 16, None, 1, 0, 8, 16, None, None, None) == 1
