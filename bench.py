@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of BAM attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  `value` is the training-shape causal forward (B=32, H=12,
+T=512, Dh=64, bf16 in / bf16 out, fp32 accumulate, SSMax on) in TFLOP/s, with one
+step = one bam_attn_fwd call (distance table + attention kernel) on inputs already
+resident in HBM.  `parts` carries the other figures the metric names: the forward at
+T=32768 (% of bf16 MFMA peak), decode against a 256,000-token KV cache (GB/s, % of
+HBM peak) and the training-shape forward+backward.  FLOPs count 4*Dh per visible
+causal (query, key) pair for the forward and 10*Dh for the backward; decode bytes are
+the K and V bytes of the kv_len visible tokens.
+
+`roofline` is for the dominant kernel of the `value` workload: its algorithmic bytes
+per launch divided by its average launch duration, measured here with HIP events
+around each launch on the stream it runs on.  `traffic` comes from the committed
+rocprofv3 counter summary in profiles/, and is null when the kernel source has changed
+since those counters were taken.  `cpu_baseline` is the fp64 oracle timed on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BAM attn fwd TFLOP/s @T=512 & 32k (% MFMA peak); decode GB/s @256k KV"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_kernel_T512_counters.json")
+FWD_SRC = os.path.join(ROOT, "positional_prior_bias_amd", "csrc", "fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, T, Dh, causal=True):
+    pairs = T * (T + 1) // 2 if causal else T * T
+    return 4.0 * Dh * B * H * pairs
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Timer:
+    """Whole-step timing (events at both ends of K steps) and per-launch event pairs."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def steps(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return e0.elapsed_time(e1) / steps, wall
+
+    def per_launch(self, fn, launches, warmup=2):
+        """Average duration of one launch of `fn`'s kernel: one event pair around `launches`
+        back-to-back launches on the stream the kernel runs on."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(launches):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / launches
+
+
+def device_inputs(torch, w, with_grad=False):
+    def d(x, bf16=True):
+        t = torch.from_numpy(x)
+        return (t.to(torch.bfloat16) if bf16 else t.to(torch.float32)).cuda()
+    out = dict(q=d(w.q), k=d(w.k), v=d(w.v), alpha=d(w.alpha, False), beta=d(w.beta, False), mu=d(w.mu, False),
+               s=d(w.s, False))
+    if with_grad:
+        out["do"] = d(w.do)
+    return out
+
+
+def bench_fwd(torch, bam, w, steps, warmup, timer, name):
+    x = device_inputs(torch, w)
+    B, H, T, Dh = w.q.shape
+    o = torch.empty((B, H, T, Dh), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bam.bam_fwd_workspace_size(B, H, T, Dh, 3), dtype=torch.uint8, device="cuda")
+
+    def call(table_ready=False):
+        bam.bam_attn_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["mu"], x["s"], causal=True, ssmax=True,
+                         o=o, lse=lse, workspace=ws, table_ready=table_ready)
+    ms, wall = timer.steps(call, steps, warmup)
+    kern_ms = timer.per_launch(lambda: call(True), max(steps, 10))
+    flops = fwd_flops(B, H, T, Dh)
+    algo_bytes = 4 * B * H * T * Dh * 2 + B * H * T * 4   # Q, K, V read + O write (bf16) + lse
+    log(f"[{name}] step {ms:.4f} ms (wall {wall:.4f}), fwd kernel {kern_ms:.4f} ms")
+    return dict(ms=ms, wall_ms=wall, kernel_ms=kern_ms, flops=flops, bytes=algo_bytes,
+                tflops=flops / ms / 1e9, kernel_tflops=flops / kern_ms / 1e9,
+                kernel_gbs=algo_bytes / kern_ms / 1e6)
+
+
+def bench_fwdbwd(torch, bam, w, steps, warmup, timer):
+    x = device_inputs(torch, w, with_grad=True)
+    B, H, T, Dh = w.q.shape
+    o = torch.empty((B, H, T, Dh), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(bam.bam_fwd_workspace_size(B, H, T, Dh, 3), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(bam.bam_bwd_workspace_size(B, H, T, Dh, 3), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        bam.bam_attn_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["mu"], x["s"], causal=True, ssmax=True,
+                         o=o, lse=lse, workspace=wsf)
+
+    def bwd():
+        bam.bam_attn_bwd(x["q"], x["k"], x["v"], o, lse, x["do"], x["alpha"], x["beta"], x["mu"], x["s"],
+                         causal=True, ssmax=True, workspace=wsb)
+
+    def step():
+        fwd()
+        bwd()
+    ms, wall = timer.steps(step, steps, warmup)
+    bwd_ms = timer.per_launch(bwd, max(steps, 10))
+    pairs = B * H * T * (T + 1) // 2
+    flops = 14.0 * Dh * pairs
+    log(f"[fwdbwd512] step {ms:.4f} ms, bwd call {bwd_ms:.4f} ms")
+    return dict(ms=ms, wall_ms=wall, bwd_call_ms=bwd_ms, flops=flops, tflops=flops / ms / 1e9,
+                bwd_tflops=10.0 * Dh * pairs / bwd_ms / 1e9)
+
+
+def bench_decode(torch, bam, w, steps, warmup, timer):
+    B, H, L, Dh = w.k.shape
+    q = torch.from_numpy(w.q).to(torch.bfloat16).cuda()
+    k, v = w.k, w.v     # already on the device (long_decode_device)
+    kv = torch.from_numpy(w.kv_len).cuda()
+    p = {n: torch.from_numpy(getattr(w, n)).cuda() for n in ("alpha", "beta", "mu", "s")}
+    o = torch.empty((B, H, Dh), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bam.bam_decode_workspace_size(B, H, L, Dh), dtype=torch.uint8, device="cuda")
+
+    def call(table_ready=False):
+        bam.bam_attn_decode(q, k, v, kv, p["alpha"], p["beta"], p["mu"], p["s"], ssmax=True, o=o, lse=lse,
+                            workspace=ws, table_ready=table_ready)
+    ms, wall = timer.steps(call, steps, warmup)
+    kern_ms = timer.per_launch(lambda: call(True), max(steps, 10))
+    nbytes = 2.0 * float(w.kv_len.astype("int64").sum()) * H * Dh * 2
+    log(f"[decode] step {ms:.4f} ms, split+combine {kern_ms:.4f} ms")
+    return dict(ms=ms, wall_ms=wall, kernels_ms=kern_ms, bytes=nbytes, gbs=nbytes / ms / 1e6,
+                kernels_gbs=nbytes / kern_ms / 1e6)
+
+
+def cpu_baseline(w, seconds):
+    """fp64 oracle on whole (b, h) heads of the same batch until `seconds` have elapsed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    B, H, T, Dh = w.q.shape
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            oracle.attn_fwd(w.q[b:b + 1, h:h + 1], w.k[b:b + 1, h:h + 1], w.v[b:b + 1, h:h + 1], w.alpha[h:h + 1],
+                            w.beta[h:h + 1], w.mu[h:h + 1], w.s[h:h + 1], causal=True, ssmax=True)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    flops = fwd_flops(1, done, T, Dh)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {B * H} (b,h) heads of the B={B},H={H},T={T},Dh={Dh} batch, every row, "
+                      f"{el:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise work single-threaded)"}
+
+
+def traffic_from_counters():
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if c.get("source_sha") != src_sha(FWD_SRC):
+        return None, "kernel changed since the counters were taken"
+    return c.get("traffic_bytes"), c.get("command")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--parts", default="fwd512,fwd32k,decode,fwdbwd512",
+                    help="comma list of fwd512,fwd32k,decode,fwdbwd512 (fwd512 is always run)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (BAM attention shards with no "
+              "exchange over heads/batch; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import positional_prior_bias_amd as bam
+    from positional_prior_bias_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    bam.lib()
+    timer = Timer(torch)
+    parts = set(args.parts.split(",")) | {"fwd512"}
+
+    log("[fwd512] generating inputs")
+    w2 = wl.training_shape()
+    r512 = bench_fwd(torch, bam, w2, args.steps, args.warmup, timer, "fwd512")
+    out_parts = {"fwd_T512": {
+        "workload": "causal fwd B=32 H=12 T=512 Dh=64 bf16, SSMax on",
+        "ms": round(r512["ms"], 5), "TFLOP/s": round(r512["tflops"], 2),
+        "pct_mfma_peak": round(100 * r512["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": round(r512["kernel_ms"], 5), "kernel_TFLOP/s": round(r512["kernel_tflops"], 2),
+        "kernel_algorithmic_GB/s": round(r512["kernel_gbs"], 1),
+        "pct_hbm_peak": round(100 * r512["kernel_gbs"] / PEAK_HBM_GBS, 2)}}
+
+    if "fwd32k" in parts:
+        log("[fwd32k] generating inputs")
+        w4 = wl.long_prefill()
+        r = bench_fwd(torch, bam, w4, max(3, args.steps // 4), 2, timer, "fwd32k")
+        out_parts["fwd_T32768"] = {
+            "workload": "causal fwd B=1 H=12 T=32768 Dh=64 bf16, 6 heavy-tailed + 6 inverted-prior heads, SSMax on",
+            "ms": round(r["ms"], 4), "TFLOP/s": round(r["tflops"], 1),
+            "pct_mfma_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+            "kernel_ms": round(r["kernel_ms"], 4), "kernel_TFLOP/s": round(r["kernel_tflops"], 1),
+            "kernel_pct_mfma_peak": round(100 * r["kernel_tflops"] / PEAK_BF16_TFLOPS, 2),
+            "roofline": {"bound": "mfma", "achieved": round(r["kernel_tflops"], 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)}}
+        del w4
+    if "decode" in parts:
+        log("[decode] generating inputs (256,000-token caches)")
+        w5 = wl.long_decode_device()
+        r = bench_decode(torch, bam, w5, max(5, args.steps // 2), 3, timer)
+        out_parts["decode_256k"] = {
+            "workload": "decode B=8 H=12 Dh=64, bf16 KV cache of 256,000 tokens, one planted key per sequence",
+            "ms": round(r["ms"], 4), "GB/s": round(r["gbs"], 1), "pct_hbm_peak": round(100 * r["gbs"] / PEAK_HBM_GBS, 2),
+            "kernels_ms": round(r["kernels_ms"], 4),
+            "roofline": {"bound": "hbm", "achieved": round(r["kernels_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(r["kernels_gbs"] / PEAK_HBM_GBS, 4),
+                         "note": "split + combine kernels (table prebuilt), K+V bytes of the visible tokens"}}
+        del w5
+    if "fwdbwd512" in parts:
+        log("[fwdbwd512] generating inputs")
+        w3 = wl.training_shape(with_grad=True)
+        r = bench_fwdbwd(torch, bam, w3, args.steps, args.warmup, timer)
+        out_parts["fwd_bwd_T512"] = {
+            "workload": "causal fwd+bwd B=32 H=12 T=512 Dh=64 bf16, dQ/dK/dV bf16 + per-head dalpha/dbeta/ds",
+            "ms": round(r["ms"], 4), "TFLOP/s": round(r["tflops"], 1),
+            "pct_mfma_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+            "bwd_call_ms": round(r["bwd_call_ms"], 4), "bwd_TFLOP/s": round(r["bwd_tflops"], 1)}
+        del w3
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[copy-calibration] copied {n} bytes 3 times")
+
+    traffic, tnote = traffic_from_counters()
+    roof = {"bound": "hbm", "achieved": round(r512["kernel_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(r512["kernel_gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": "fwd_bf16_kernel<64,causal>",
+            "algorithmic_bytes_per_launch": r512["bytes"],
+            "kernel_ms": round(r512["kernel_ms"], 5)}
+    if traffic is None:
+        roof["traffic_note"] = tnote
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[cpu_baseline] oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(w2, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(r512["tflops"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r512["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, per-head prior parameters as documented)",
+        "config": {"workload": "training-shape causal BAM attention forward, B=32 H=12 T=512 Dh=64, bf16 in/out, "
+                               "fp32 accumulate, SSMax on; one step = bam_attn_fwd (distance table + attention)",
+                   "B": 32, "H": 12, "T": 512, "Dh": 64, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "parts": out_parts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -72,6 +72,11 @@ typedef int bam_status;
 /* flags */
 #define BAM_CAUSAL 1u   /* key j visible to query i only when j <= i */
 #define BAM_SSMAX  2u   /* multiply the logits of query i by c_i = s_h ln(n_i) */
+/* The workspace already holds the distance table written by an earlier call with the same
+ * alpha, beta, mu, shape and flags (and the same workspace): skip rebuilding it.  For
+ * callers whose prior parameters do not change between calls (inference); with trained
+ * parameters leave it unset.  Accepted by bam_attn_fwd and bam_attn_decode. */
+#define BAM_TABLE_READY 4u
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* bam_status_string(bam_status status);

@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BamError", "lib", "lib_path",
+    "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BamError", "lib", "lib_path",
     "bam_prior_table", "bam_attn_fwd", "bam_attn_decode", "bam_attn_bwd",
     "bam_fwd_workspace_size", "bam_decode_workspace_size", "bam_bwd_workspace_size",
     "EXPORTED_SYMBOLS",
@@ -23,6 +23,7 @@ BAM_BF16 = 0
 BAM_F32 = 1
 BAM_CAUSAL = 1
 BAM_SSMAX = 2
+BAM_TABLE_READY = 4
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -178,11 +179,15 @@ def bam_prior_table(alpha, beta, mu, d0: int, n: int, derivatives: bool = False,
 
 
 def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True, o_dtype=None,
-                 o=None, lse=None, workspace=None, stream=None):
-    """Prefill forward; q, k, v [B, H, T, Dh].  Returns (o, lse)."""
+                 o=None, lse=None, workspace=None, stream=None, table_ready=False):
+    """Prefill forward; q, k, v [B, H, T, Dh].  Returns (o, lse).
+
+    table_ready: the given workspace already holds this call's distance table (BAM_TABLE_READY)."""
     torch = _torch()
     B, H, T, Dh = q.shape
-    flags = _flags(causal, ssmax)
+    flags = _flags(causal, ssmax) | (BAM_TABLE_READY if table_ready else 0)
+    if table_ready and workspace is None:
+        raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != q.shape or v.shape != q.shape:
         raise BamError("q, k, v must share shape and dtype")
@@ -193,7 +198,7 @@ def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
         oc = _dtype_code(o)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    nb = bam_fwd_workspace_size(B, H, T, Dh, flags)
+    nb = bam_fwd_workspace_size(B, H, T, Dh, flags & ~BAM_TABLE_READY)
     ws = _workspace(nb, q.device, workspace)
     a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
     st = lib().bam_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), in_code, B, H, T, Dh, a, b_, m_, s_,
@@ -204,11 +209,13 @@ def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
 
 
 def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, ssmax=True, o_dtype=None,
-                    o=None, lse=None, workspace=None, stream=None):
+                    o=None, lse=None, workspace=None, stream=None, table_ready=False):
     """Decode; q [B, H, Dh], caches [B, H, Lmax, Dh], kv_len int32 [B].  Returns (o, lse)."""
     torch = _torch()
     B, H, Lmax, Dh = k_cache.shape
-    flags = _flags(False, ssmax)
+    flags = _flags(False, ssmax) | (BAM_TABLE_READY if table_ready else 0)
+    if table_ready and workspace is None:
+        raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(k_cache)
     if kv_len.dtype != torch.int32:
         raise BamError("kv_len must be int32")

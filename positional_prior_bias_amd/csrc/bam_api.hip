@@ -82,7 +82,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       lse == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY)) != 0) return BAM_EINVAL;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   if (in_dtype == BAM_BF16) {
     if (Dh != 32 && Dh != 64 && Dh != 128) return BAM_EUNSUPPORTED;
@@ -98,8 +98,11 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   const TableGeom g = table_geom(T, causal);
   hipStream_t st = (hipStream_t)stream;
   float* tab = (float*)workspace;
-  hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr, st);
-  if (e != hipSuccess) return BAM_EHIP;
+  hipError_t e = hipSuccess;
+  if (!(flags & BAM_TABLE_READY)) {
+    e = bam::launch_prior_table(alpha, beta, mu, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr, st);
+    if (e != hipSuccess) return BAM_EHIP;
+  }
   bam::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -153,15 +156,17 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
       !aligned16(o) || lse == nullptr || kv_len == nullptr || workspace == nullptr ||
       !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   const DecodeLayout L = decode_layout(B, H, Lmax, Dh);
   if (workspace_bytes < L.total) return BAM_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   float* tab = (float*)((char*)workspace + L.tab_off);
-  hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, 0, Lmax, L.tab_stride, 1.0f, tab, nullptr, nullptr, st);
-  if (e != hipSuccess) return BAM_EHIP;
+  if (!(flags & BAM_TABLE_READY)) {
+    hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, 0, Lmax, L.tab_stride, 1.0f, tab, nullptr, nullptr, st);
+    if (e != hipSuccess) return BAM_EHIP;
+  }
   bam::DecodeArgs a;
   a.q = q;
   a.k = k_cache;

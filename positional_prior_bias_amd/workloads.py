@@ -35,13 +35,15 @@ SSMAX = 2
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even).
 
-    Returns a float32 array whose values are exactly representable in bf16.
-    Inputs here are finite standard-normal draws, so NaN handling is not needed.
+    Returns a float32 array whose values are exactly representable in bf16.  Inputs
+    here are finite draws, so the 32-bit add cannot overflow and NaN handling is not
+    needed.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(x.shape)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -223,3 +225,43 @@ def alibi_slopes(H: int) -> np.ndarray:
     schedule to every head count, power of two or not).
     """
     return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], np.float64)
+
+
+def long_decode_device(seed: int = 4, B: int = 8, H: int = 12, L: int = 256000, Dh: int = 64,
+                       head_seed: int = 3, kv_len: np.ndarray | None = None, device="cuda") -> Workload:
+    """Decode workload with the KV caches drawn directly on the GPU (256k-token caches).
+
+    K and V ([B, H, L, Dh], bf16) come from torch's counter-based Philox generator on
+    `device`, seeded with `seed`: for each sequence b, K[b] is one float32 randn draw of
+    (H, L, Dh) rounded to bf16, then V[b] likewise, b = 0, 1, ...  q (B, H, Dh) and the
+    planted positions come from numpy default_rng(seed) as in long_decode; the planted key
+    of sequence b is k_p <- bf16(k_p + 8 q / |q|) in every head.  The returned workload's
+    k and v are torch device tensors; everything else is numpy.  Head parameters are those
+    of the long prefill.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    k = torch.empty((B, H, L, Dh), dtype=torch.bfloat16, device=device)
+    v = torch.empty((B, H, L, Dh), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        k[b] = torch.randn((H, L, Dh), generator=gen, dtype=torch.float32, device=device).to(torch.bfloat16)
+        v[b] = torch.randn((H, L, Dh), generator=gen, dtype=torch.float32, device=device).to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (B, H, Dh), True)
+    if kv_len is None:
+        kv_len = np.full(B, L, np.int32)
+    kv_len = np.asarray(kv_len, np.int32)
+    planted = np.array([rng.integers(0, kv_len[b]) for b in range(B)], np.int64)
+    for b in range(B):
+        p = int(planted[b])
+        dirs = q[b].astype(np.float64)
+        dirs = 8.0 * dirs / np.linalg.norm(dirs, axis=1, keepdims=True)
+        row = k[b, :, p].to(torch.float64) + torch.from_numpy(dirs).to(device)
+        k[b, :, p] = row.to(torch.float32).to(torch.bfloat16)
+    hrng = np.random.default_rng(head_seed)
+    for _ in range(3):
+        hrng.standard_normal(size=(1, H, 32768, Dh), dtype=np.float32)
+    alpha, beta, mu, s = extrapolation_heads(hrng, H)
+    return Workload("decode_L%d_device" % L, B, H, L, Dh, "bf16", SSMAX, alpha, beta, mu, s, q, k, v,
+                    kv_len=kv_len, planted=planted)

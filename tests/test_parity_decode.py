@@ -69,10 +69,22 @@ def test_decode_repeatable_and_bf16_output():
 
 
 def test_decode_full_context_256k():
-    """B=8, H=12, Dh=64, 256,000-token bf16 caches with one planted key per sequence."""
-    w = wl.long_decode()
-    o, lse = run_decode(w)
-    O, LS = oracle.attn_decode(w.q, w.k, w.v, w.kv_len, w.alpha, w.beta, w.mu, w.s, ssmax=True)
+    """B=8, H=12, Dh=64, 256,000-token bf16 caches (drawn on the device) with one planted key
+    per sequence; every (b, h) checked against the oracle on the same cache values."""
+    torch = torch_mod()
+    w = wl.long_decode_device()
+    p = params(w)
+    kv = torch.from_numpy(w.kv_len).cuda()
+    o, lse = _bam().bam_attn_decode(dev(w.q, "bf16"), w.k, w.v, kv, p["alpha"], p["beta"], p["mu"], p["s"],
+                                    ssmax=True, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O = np.empty((w.B, w.H, w.Dh))
+    LS = np.empty((w.B, w.H))
+    for b in range(w.B):
+        kb = w.k[b].float().cpu().numpy()[None]
+        vb = w.v[b].float().cpu().numpy()[None]
+        Ob, Lb = oracle.attn_decode(w.q[b:b + 1], kb, vb, w.kv_len[b:b + 1], w.alpha, w.beta, w.mu, w.s, ssmax=True)
+        O[b], LS[b] = Ob[0], Lb[0]
     err_o, err_l = max_abs(host(o), O), max_abs(host(lse), LS)
     print(f"decode 256k: max|dO|={err_o:.3e} max|dlse|={err_l:.3e}")
     assert err_o <= BF16_O_ABS
