@@ -5,7 +5,9 @@
 Every HIP source under csrc/ is compiled with hipcc for gfx950 only, then linked
 into positional_prior_bias_amd/libbam.so.  Packed fp32 VALU instructions are
 disabled on the device side (``-packed-fp32-ops``); hipcc's host pass prints a
-harmless warning that it does not know that feature.
+harmless warning that it does not know that feature.  ``-fno-honor-nans`` lets
+max/min lower to single instructions: no kernel here produces a NaN (masked
+logits are -inf and every exp2 argument is guarded against -inf - -inf).
 """
 from __future__ import annotations
 
@@ -24,6 +26,7 @@ ARCH = "gfx950"
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
 

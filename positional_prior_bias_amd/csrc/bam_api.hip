@@ -42,6 +42,17 @@ bool prior_ok(const float* alpha, const float* beta, const float* s, unsigned fl
   return true;
 }
 
+// bf16 forward table: reversed, padded with -inf by kFwdTabPad on each side, sqrt(Dh)-scaled
+// (entry u holds d = dhi + kFwdTabPad - u).  The fp32 path uses the plain table.
+TableGeom fwd_table_geom(int T, bool causal) {
+  const TableGeom g = table_geom(T, causal);
+  TableGeom r;
+  r.d0 = (T - 1) + bam::kFwdTabPad;   // distance held at entry 0
+  r.n = g.n + 2 * bam::kFwdTabPad;
+  r.stride = pad64(r.n);
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,7 +82,8 @@ size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags) {
   (void)B;
   (void)Dh;
   if (H <= 0 || T <= 0) return 0;
-  const TableGeom g = table_geom(T, (flags & BAM_CAUSAL) != 0);
+  const bool causal = (flags & BAM_CAUSAL) != 0;
+  const TableGeom g = fwd_table_geom(T, causal);
   return align_up((size_t)H * g.stride * sizeof(float));
 }
 
@@ -95,12 +107,17 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (workspace_bytes < bam_fwd_workspace_size(B, H, T, Dh, flags)) return BAM_EWORKSPACE;
 
   const bool causal = (flags & BAM_CAUSAL) != 0;
-  const TableGeom g = table_geom(T, causal);
+  const bool bf16 = in_dtype == BAM_BF16;
+  const TableGeom g = bf16 ? fwd_table_geom(T, causal) : table_geom(T, causal);
   hipStream_t st = (hipStream_t)stream;
   float* tab = (float*)workspace;
   hipError_t e = hipSuccess;
   if (!(flags & BAM_TABLE_READY)) {
-    e = bam::launch_prior_table(alpha, beta, mu, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr, st);
+    if (bf16)
+      e = bam::launch_prior_table_ex(alpha, beta, mu, H, g.d0, -1, g.n, g.stride, causal ? 0 : -(T - 1), T - 1,
+                                     std::sqrt((float)Dh), tab, nullptr, nullptr, st);
+    else
+      e = bam::launch_prior_table(alpha, beta, mu, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr, st);
     if (e != hipSuccess) return BAM_EHIP;
   }
   bam::FwdArgs a;
@@ -119,7 +136,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   a.o = o;
   a.o_f32 = o_dtype == BAM_F32;
   a.lse = lse;
-  e = in_dtype == BAM_BF16 ? bam::launch_fwd_bf16(a, Dh, st) : bam::launch_fwd_f32(a, Dh, st);
+  e = bf16 ? bam::launch_fwd_bf16(a, Dh, st) : bam::launch_fwd_f32(a, Dh, st);
   return hip_status(e);
 }
 

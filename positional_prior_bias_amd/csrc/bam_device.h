@@ -30,6 +30,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1), fp32 accumulate)
+__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -43,6 +50,13 @@ __device__ __forceinline__ float ssmax_c(bool ssmax, float s, int n) {
 
 // Lane exchange with lane ^ 32 (the other half of a wave64).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max(x, x of lane ^ 32) without an LDS round trip: v_permlane32_swap of x with itself
+// leaves, in each lane, one copy of its own value and one of its partner's.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 }  // namespace bam
 

@@ -11,12 +11,22 @@ namespace bam {
 hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
                               int n, int stride, float scale, float* tab, float* dalpha, float* dbeta,
                               hipStream_t stream);
+// General form: entry t holds d = d_first + step * t; entries with d outside [dlo, dhi]
+// are padding (-inf bias, zero derivatives).  The bias is multiplied by `scale`.
+hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, int H, int d_first,
+                                 int step, int n, int stride, int dlo, int dhi, float scale, float* tab,
+                                 float* dalpha, float* dbeta, hipStream_t stream);
+
+// Forward distance table: reversed (entry u holds d = dhi + kFwdTabPad - u), padded by
+// kFwdTabPad entries of -inf on both sides and scaled by sqrt(Dh), so every per-tile
+// window of the forward kernel is one contiguous, in-bounds copy.
+constexpr int kFwdTabPad = 320;
 
 struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* tab;   // [H][tab_stride] natural-unit bias, index = d - tab_d0
+  const float* tab;   // bf16 path: reversed padded sqrt(Dh)-scaled table; fp32 path: b(d) at d - tab_d0
   const float* s;     // SSMax strength per head (NULL without SSMax)
   int tab_d0;         // distance held at index 0
   int tab_stride;     // floats per head row

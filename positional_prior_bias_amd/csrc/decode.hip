@@ -176,29 +176,53 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// Merge the per-range partials of one (b, h): M = max m_s, L = sum 2^(m_s - M) l_s,
+// O = sum 2^(m_s - M) o_s / L.  Four waves take every fourth range (independent loads,
+// unrolled), then combine through LDS.
 template <int DH>
-__global__ void __launch_bounds__(DH) decode_combine_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
+  constexpr int EPL = DH / 64;   // head-dim entries per lane
+  __shared__ float smax[4];
+  __shared__ float sl[4];
+  __shared__ float so[4][DH];
   const int bh = blockIdx.x;
-  const int e = threadIdx.x;
-  const float* part = a.part + (size_t)bh * a.nsplit * (DH + 2);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int S = a.nsplit;
+  const float* part = a.part + (size_t)bh * S * (DH + 2);
   float M = kNegInf;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[(size_t)s * (DH + 2)]);
-  float Ls = 0.f, Os = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
+  for (int s = tid; s < S; s += 256) M = fmaxf(M, part[(size_t)s * (DH + 2)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) smax[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  float L = 0.f, O[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) O[e] = 0.f;
+#pragma unroll 4
+  for (int s = wave; s < S; s += 4) {
     const float* ps = part + (size_t)s * (DH + 2);
     const float ms = ps[0];
-    if (ms == kNegInf) continue;
-    const float wt = exp2_fast(ms - M);
-    Ls += wt * ps[1];
-    Os += wt * ps[2 + e];
+    const float wt = (ms == kNegInf) ? 0.f : exp2_fast(ms - M);
+    L = fmaf(wt, ps[1], L);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[e] = fmaf(wt, ps[2 + lane + 64 * e], O[e]);
   }
-  const float out = Os / Ls;
-  if (a.o_f32) {
-    ((float*)a.o)[(size_t)bh * DH + e] = out;
-  } else {
-    ((__bf16*)a.o)[(size_t)bh * DH + e] = (__bf16)out;
+  if (lane == 0) sl[wave] = L;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) so[wave][lane + 64 * e] = O[e];
+  __syncthreads();
+  if (tid < DH) {
+    const float Ls = sl[0] + sl[1] + sl[2] + sl[3];
+    const float out = (so[0][tid] + so[1][tid] + so[2][tid] + so[3][tid]) / Ls;
+    if (a.o_f32) {
+      ((float*)a.o)[(size_t)bh * DH + tid] = out;
+    } else {
+      ((__bf16*)a.o)[(size_t)bh * DH + tid] = (__bf16)out;
+    }
+    if (tid == 0) a.lse[bh] = (M + __log2f(Ls)) * kLn2;
   }
-  if (e == 0) a.lse[bh] = (M + __log2f(Ls)) * kLn2;
 }
 
 template <int DH>
@@ -206,7 +230,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(decode_split_kernel<DH>, dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3(a.B * a.H), dim3(DH), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3(a.B * a.H), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -7,14 +7,21 @@
 // the exact result of the dense definition up to float rounding.
 //
 // bf16 kernel design (wave64, v_mfma_f32_32x32x16_bf16):
-//   * A work-group of 4 waves owns 128 query rows of one (b, h); each wave owns 32.
+//   * A work-group of 4 waves owns 256 query rows of one (b, h) (128 for Dh = 128); each
+//     wave owns 64 rows as two 32-row blocks that share every K and V^T operand read.
+//   * Key tiles of 64 are double-buffered in LDS: the next tile is loaded from HBM into
+//     registers while the current one is computed, then stored; one barrier per tile.
 //   * S^T = K Q^T is computed with keys as MFMA rows and queries as columns, so each
 //     lane owns one query (column) and 16 keys per 32x32 block; the row max / sum of
 //     the softmax is an in-lane reduction plus one exchange with lane ^ 32.
 //   * The bias enters as the MFMA accumulator's initial value: the accumulator is
 //     loaded with sqrt(Dh) * b(i - j) from a window of the per-head distance table
-//     staged in LDS, so the MFMA returns q.k + sqrt(Dh) b directly.  Distances the
-//     causal mask forbids hold -inf in that window, so masking is free as well.
+//     staged in LDS (stored in reverse distance order, so a lane's 16 values are read
+//     in register order), and the MFMA returns q.k + sqrt(Dh) b directly.  Distances
+//     the causal mask forbids hold -inf in that window, so masking is free as well.
+//   * The running max is rescaled lazily: O and l are rescaled only when a row max
+//     grows by more than 2^8, otherwise the old max is kept (p <= 2^8 is exact enough
+//     in fp32 accumulators and bf16 P).
 //   * O^T = V^T P^T: P^T is fed from the S^T accumulators without any lane exchange
 //     by letting the MFMA's contraction index run over the keys in the order the
 //     accumulator holds them; V is staged transposed in LDS to match.
@@ -29,22 +36,72 @@ namespace bam {
 
 namespace {
 
-constexpr int kMQ = 128;   // query rows per work-group (4 waves x 32)
 constexpr int kNK = 64;    // keys per tile
-constexpr int kTW = kMQ + kNK;  // distance-window entries per tile
 
-__device__ __forceinline__ int swz(int r, int mask) { return (r ^ (r >> 1)) & mask; }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define BAM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int DH, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
-  constexpr int KCH = DH / 8;          // 16-byte chunks per K row
-  constexpr int KS = DH / 16;          // MFMA k-steps over the head dimension
-  constexpr int DB = DH / 32;          // 32-row blocks of O^T
-  constexpr int VTS = kNK + 4;         // bf16 per V^T row (padded against bank conflicts)
+// Direct HBM -> LDS copies (no VGPR staging): lane l writes lds_base + size * l.
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, BAM_LDS(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, BAM_LDS(lds_base), 4, 0, 0);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kNK * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DH * VTS];
-  __shared__ float tw[kTW];
+// Transposing LDS read (gfx950): in each group of 16 lanes, lane i receives element i of
+// the 4-element rows read by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Row swizzle of the 16-byte chunks of a 128-byte (Dh = 64) row in LDS: with m = row / 2,
+// s = m ^ ((m & 1) << 2).  The 16 rows read by 16 lanes of a K operand read then hit 16
+// distinct chunk slots of the 256-byte bank space, and the 4 rows x 4 chunks of each half
+// wave of a transposing V read do too.  Other head sizes use the Gray code of the row.
+template <int DH>
+__device__ __forceinline__ int vswz(int r) {
+  if (DH == 64) {
+    const int mm = r >> 1;
+    return (mm ^ ((mm & 1) << 2)) & 7;
+  }
+  return swz_chunk(r, DH / 8 - 1);
+}
+
+// Four copies of the reversed distance window, copy c shifted by c entries, so every lane
+// reads its runs of 4 consecutive distances with one aligned 16-byte load.  Copies are
+// TW + 16 floats apart: copy c then starts at 16-byte bank group 4 c, and the 16 lanes of
+// one LDS cycle (4 consecutive groups of 4 lanes, each lane group spanning the 4 copies)
+// hit 16 distinct bank groups.
+template <int DH, int TW>
+struct FwdTile {
+  uint16_t k[kNK * DH];
+  uint16_t v[kNK * DH];
+  float w[4][TW + 16];
+};
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt / lgkmcnt left at max)
+#define BAM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
+// operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
+template <int DH, bool CAUSAL, int NQB>
+__global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a, int nqb) {
+  constexpr int QW = 32 * NQB;          // query rows per wave
+  constexpr int MQ = 4 * QW;            // query rows per work-group
+  constexpr int TW = MQ + kNK;          // distance-window entries per tile (multiple of 64)
+  constexpr int KCH = DH / 8;           // 16-byte chunks per K / V row
+  constexpr int KS = DH / 16;           // MFMA k-steps over the head dimension
+  constexpr int DB = DH / 32;           // 32-row blocks of O^T
+  constexpr int CPW = kNK * KCH / 256;  // 1 KiB direct loads per wave per tensor
+  constexpr int WPW = TW / 64;          // window loads per wave (4 copies x TW/64 over 4 waves)
+  constexpr int LPT = 2 * CPW + WPW;    // direct-load instructions per wave per tile
+  constexpr float kLazy = 8.0f;         // rescale only when a row max grows by > 2^8
+  static_assert(kNK * KCH % 256 == 0, "tile must split into 1 KiB wave loads");
+  static_assert(LPT < 64, "vmcnt range");
+
+  // three buffers as distinct objects: the tile being read, and up to two being filled
+  __shared__ __attribute__((aligned(16))) FwdTile<DH, TW> tA, tB, tC;
 
   const int BH = a.B * a.H;
   const int bid = blockIdx.x;
@@ -63,168 +120,241 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   const int wave = tid >> 6;
   const int ql = lane & 31;
   const int hh = lane >> 5;
-  const int i0 = qb * kMQ;
-  const int i = i0 + wave * 32 + ql;
+  const int i0 = qb * MQ;
+  const int iw = i0 + wave * QW;        // first query row of this wave
 
-  // Q^T operand: lane holds q_i[16 ks + 8 hh .. + 7]
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (i < T) w = *(const u32x4*)(Q + (size_t)i * DH + 16 * ks + 8 * hh);
-    qf[ks] = as_bf16x8(w);
-  }
-
+  // Q^T operands: lane holds q_i[16 ks + 8 hh .. + 7] of its query in each block
+  bf16x8 qf[NQB][KS];
+  float Cl[NQB], m[NQB], l[NQB], lr[NQB];
   const float sqrtD = __builtin_sqrtf((float)DH);
-  const int n_i = CAUSAL ? i + 1 : T;
-  const float c = ssmax_c(a.ssmax, a.ssmax ? a.s[h] : 1.0f, n_i);
-  // logit in log2 units = Cl * (q.k + sqrt(Dh) b); c = 0 only when one key is visible
-  const float Cl = fmaxf(c * kLog2e / sqrtD, FLT_MIN);
-
-  f32x16 oacc[DB];
+  const float sh = a.ssmax ? a.s[h] : 1.0f;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb2 = 0; qb2 < NQB; ++qb2) {
+    const int i = iw + 32 * qb2 + ql;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) oacc[db][x] = 0.f;
-  float m = kNegInf, l = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (i < T) w = *(const u32x4*)(Q + (size_t)i * DH + 16 * ks + 8 * hh);
+      qf[qb2][ks] = as_bf16x8(w);
+    }
+    const float c = ssmax_c(a.ssmax, sh, CAUSAL ? i + 1 : T);
+    // logit in log2 units = Cl * (q.k + sqrt(Dh) b); c = 0 only when one key is visible
+    Cl[qb2] = fmaxf(c * kLog2e / sqrtD, FLT_MIN);
+    m[qb2] = kNegInf;
+    l[qb2] = 0.f;
+    lr[qb2] = 0.f;
+  }
+  f32x16 oacc[NQB][DB];
+#pragma unroll
+  for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) oacc[qb2][db][x] = 0.f;
 
-  const int kend = CAUSAL ? min(T, i0 + kMQ) : T;
+  const int kend = CAUSAL ? min(T, i0 + MQ) : T;
   const int ntiles = (kend + kNK - 1) / kNK;
   const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
-  const int dlo = CAUSAL ? 0 : -(T - 1);
-  const int dhi = T - 1;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kNK;
-    __syncthreads();
-    // ---- stage K (row-major, swizzled 16-byte chunks)
-#pragma unroll
-    for (int cidx = tid; cidx < kNK * KCH; cidx += 256) {
-      const int r = cidx / KCH;
-      const int ch = cidx - r * KCH;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (j0 + r < T) val = *(const u32x4*)(K + (size_t)(j0 + r) * DH + ch * 8);
-      *(u32x4*)(Ks + r * DH + (ch ^ swz(r, KCH - 1)) * 8) = val;
-    }
-    // ---- stage V transposed: Vt[dh][key], two keys per dword
-#pragma unroll
-    for (int pidx = tid; pidx < (kNK / 2) * KCH; pidx += 256) {
-      const int p = pidx % (kNK / 2);
-      const int ch = pidx / (kNK / 2);
-      const int r0 = 2 * p;
-      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-      if (j0 + r0 < T) v0 = *(const u32x4*)(V + (size_t)(j0 + r0) * DH + ch * 8);
-      if (j0 + r0 + 1 < T) v1 = *(const u32x4*)(V + (size_t)(j0 + r0 + 1) * DH + ch * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = v0[e >> 1], w1 = v1[e >> 1];
-        // even e: low halves of w0 / w1; odd e: high halves
-        const uint32_t packed = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                        : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-        *(uint32_t*)(Vt + (ch * 8 + e) * VTS + r0) = packed;
-      }
-    }
-    // ---- stage the distance window: tw[x] = sqrt(Dh) * b(d_min + x)
-    const int d_min = i0 - j0 - (kNK - 1);
-    for (int x = tid; x < kTW; x += 256) {
-      const int d = d_min + x;
-      float val = kNegInf;
-      if (d >= dlo && d <= dhi) val = sqrtD * tabh[d - a.tab_d0];
-      tw[x] = val;
-    }
-    __syncthreads();
+  // window value index y of this lane's first accumulator group; the four values of each
+  // group are consecutive, read with one 16-byte load from copy (y & 3)
+  const int ybase = (MQ - 1) - (QW * wave + ql) + 4 * hh;   // + 32 (kb - qb2) + 8 g
+  const int wcopy = ybase & 3;
 
-    // ---- S'^T = K Q^T + sqrt(Dh) b   (two 32-key blocks)
-    f32x16 sacc[2];
+  // ---- issue the direct loads of key tile j0.  Chunk position p of K / V holds global
+  // chunk (row, (p % KCH) ^ swizzle(row)); rows past T are clamped to T - 1 (in bounds;
+  // those keys are masked by the table or explicitly).  Every wave issues LPT loads.
+  auto issue_tile = [&](FwdTile<DH, TW>& tl, int j0) {
+#pragma unroll
+    for (int r = 0; r < CPW; ++r) {
+      const int p0 = (wave * CPW + r) * 64;
+      const int p = p0 + lane;
+      const int row = p / KCH;
+      const int gc = (p % KCH) ^ vswz<DH>(row);
+      const size_t off = (size_t)min(j0 + row, T - 1) * DH + gc * 8;
+      g2lds16(K + off, &tl.k[p0 * 8]);
+      g2lds16(V + off, &tl.v[p0 * 8]);
+    }
+    const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
+#pragma unroll
+    for (int r = 0; r < WPW; ++r) {
+      const int x = wave * WPW + r;         // 0 .. 4 * TW / 64 - 1
+      const int cpy = x / (TW / 64), seg = x % (TW / 64);
+      g2lds4(tabh + u0 + cpy + 64 * seg + lane, &tl.w[cpy][64 * seg]);
+    }
+  };
+
+  auto compute_tile = [&](const FwdTile<DH, TW>& tl, int j0) {
+    // a wave whose rows all precede this tile's keys has nothing to do (causal)
+    if (CAUSAL && j0 > iw + QW - 1) return;
+    // ---- S'^T = K Q^T + sqrt(Dh) b: each accumulator starts from its bias block (read
+    // straight into the accumulator registers), then accumulates the contraction.  All
+    // LDS reads of the phase are issued before the first MFMA so their latency overlaps.
+    const f32x4* __restrict__ wv = (const f32x4*)tl.w[wcopy];
+    f32x16 sacc[NQB][2];
+    u32x4 kw[2][KS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int kl = 32 * kb + 8 * (x >> 2) + 4 * hh + (x & 3);
-        sacc[kb][x] = tw[32 * wave + ql + (kNK - 1) - kl];
+      for (int qb2 = 0; qb2 < NQB; ++qb2) {
+        const int y4 = ((ybase - wcopy) >> 2) + 8 * (kb - qb2);   // 16-byte units
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v4 = wv[y4 + 2 * g];
+          sacc[qb2][kb][4 * g + 0] = v4[0];
+          sacc[qb2][kb][4 * g + 1] = v4[1];
+          sacc[qb2][kb][4 * g + 2] = v4[2];
+          sacc[qb2][kb][4 * g + 3] = v4[3];
+        }
       }
       const int r = 32 * kb + ql;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = 2 * ks + hh;
-        const u32x4 kw = *(const u32x4*)(Ks + r * DH + (ch ^ swz(r, KCH - 1)) * 8);
-        sacc[kb] = mfma32x32x16(as_bf16x8(kw), qf[ks], sacc[kb]);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        kw[kb][ks] = *(const u32x4*)(&tl.k[r * DH + ((2 * ks + hh) ^ vswz<DH>(r)) * 8]);
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qb2 = 0; qb2 < NQB; ++qb2)
+          sacc[qb2][kb] = mfma32x32x16(as_bf16x8(kw[kb][ks]), qf[qb2][ks], sacc[qb2][kb]);
     if (!CAUSAL && j0 + kNK > T) {
+#pragma unroll
+      for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int kl = 32 * kb + 8 * (x >> 2) + 4 * hh + (x & 3);
+            if (j0 + kl >= T) sacc[qb2][kb][x] = kNegInf;
+          }
+    }
+
+    // ---- online softmax (exp2 domain) with lazy rescaling
+    u32x4 pf[NQB][4];
+#pragma unroll
+    for (int qb2 = 0; qb2 < NQB; ++qb2) {
+      float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int kl = 32 * kb + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (j0 + kl >= T) sacc[kb][x] = kNegInf;
+        for (int x = 0; x < 16; x += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[qb2][kb][x], sacc[qb2][kb][x + 1]));
+      mx = max_xor32(mx);
+      const float cand = Cl[qb2] * mx;
+      if (__any(cand > m[qb2] + kLazy)) {
+        const float m_new = fmaxf(m[qb2], cand);
+        const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(m[qb2] - m_new);
+        m[qb2] = m_new;
+        l[qb2] *= sc;
+        lr[qb2] *= sc;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) oacc[qb2][db][x] *= sc;
+      }
+      const float m_use = (m[qb2] == kNegInf) ? 0.f : m[qb2];
+      // lr sums the same bf16-rounded weights the PV product uses (v_dot2 with (1, 1)):
+      // O is normalised by it, an exact convex combination of the rows of V under those
+      // weights.  l sums the fp32 weights and gives lse.
+      float ls[2] = {0.f, 0.f}, le[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; x += 2) {
+          const float p0 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x], -m_use));
+          const float p1 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x + 1], -m_use));
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          pf[qb2][2 * kb + (x >> 3)][(x & 7) >> 1] = pk;
+          ls[(x >> 1) & 1] = sum_bf16x2(pk, ls[(x >> 1) & 1]);
+          le[(x >> 1) & 1] += p0 + p1;
         }
+      lr[qb2] += ls[0] + ls[1];
+      l[qb2] += le[0] + le[1];
     }
 
-    // ---- online softmax (exp2 domain)
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[kb][x]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, Cl * mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float sc = exp2_fast(m - m_use);
-    m = m_new;
-    l *= sc;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) oacc[db][x] *= sc;
-
-    u32x4 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; x += 2) {
-        const float p0 = exp2_fast(Cl * sacc[kb][x] - m_use);
-        const float p1 = exp2_fast(Cl * sacc[kb][x + 1] - m_use);
-        l += p0 + p1;
-        pf[2 * kb + (x >> 3)][(x & 7) >> 1] = pack_bf16x2(p0, p1);
-      }
-
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T.  The V^T operand of lane (dh, hh) holds keys
+    // {16 st + 4 hh + 0..3, + 8 .. + 11} of column dh: two transposing reads of the
+    // row-major V tile (lane i of 16-lane group G reads row key0 + i / 4, columns
+    // dh0 + 4 (i % 4) .. + 3, dh0 = 32 db + 16 (G % 2)).
+    const int G = lane >> 4, gi = lane & 15;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int row = 32 * db + ql;
+      const int col = 32 * db + 16 * (G & 1) + 4 * (gi & 3);
+      bf16x8 av[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int col = 16 * st + 4 * hh;   // = 32 kb + 16 s' + 4 hh
-        const u32x2 lo = *(const u32x2*)(Vt + row * VTS + col);
-        const u32x2 hi = *(const u32x2*)(Vt + row * VTS + col + 8);
-        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma32x32x16(as_bf16x8(av), as_bf16x8(pf[st]), oacc[db]);
+        const int r0 = 16 * st + 4 * (G >> 1) + (gi >> 2);
+        const int r1 = r0 + 8;
+        const s16x4 v0 = lds_read_tr16(&tl.v[r0 * DH + (((col >> 3) ^ vswz<DH>(r0)) << 3) + (col & 7)]);
+        const s16x4 v1 = lds_read_tr16(&tl.v[r1 * DH + (((col >> 3) ^ vswz<DH>(r1)) << 3) + (col & 7)]);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        av[st] = __builtin_bit_cast(bf16x8, vv);
       }
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int qb2 = 0; qb2 < NQB; ++qb2)
+          oacc[qb2][db] = mfma32x32x16(av[st], as_bf16x8(pf[qb2][st]), oacc[qb2][db]);
     }
+  };
+
+  // ---- three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load
+  issue_tile(tA, 0);
+  if (ntiles > 1) {
+    issue_tile(tB, kNK);
+    BAM_WAIT_VMCNT(LPT);    // tile 0 landed (tile 1 may still be in flight)
+  } else {
+    BAM_WAIT_VMCNT(0);
+  }
+  __syncthreads();
+  // wait for tile t + 1 (tile t + 2 may still be in flight) and publish it
+  auto advance = [&](int t) {
+    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
+    else BAM_WAIT_VMCNT(0);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 3) {
+    if (t + 2 < ntiles) issue_tile(tC, (t + 2) * kNK);
+    compute_tile(tA, t * kNK);
+    advance(t);
+    if (t + 1 >= ntiles) break;
+    if (t + 3 < ntiles) issue_tile(tA, (t + 3) * kNK);
+    compute_tile(tB, (t + 1) * kNK);
+    advance(t + 1);
+    if (t + 2 >= ntiles) break;
+    if (t + 4 < ntiles) issue_tile(tB, (t + 4) * kNK);
+    compute_tile(tC, (t + 2) * kNK);
+    advance(t + 2);
   }
 
   // ---- epilogue
-  const float lt = l + xor32(l);
-  if (i < T) {
-    const float inv = 1.0f / lt;
-    const size_t orow = base + (size_t)i * DH;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb2 = 0; qb2 < NQB; ++qb2) {
+    const int i = iw + 32 * qb2 + ql;
+    const float lt = l[qb2] + xor32(l[qb2]);
+    const float lrt = lr[qb2] + xor32(lr[qb2]);
+    if (i < T) {
+      const float inv = 1.0f / lrt;
+      const size_t orow = base + (size_t)i * DH;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dh0 = 32 * db + 8 * g + 4 * hh;
-        const float o0 = oacc[db][4 * g + 0] * inv, o1 = oacc[db][4 * g + 1] * inv;
-        const float o2 = oacc[db][4 * g + 2] * inv, o3 = oacc[db][4 * g + 3] * inv;
-        if (a.o_f32) {
-          f32x4 w = {o0, o1, o2, o3};
-          *(f32x4*)((float*)a.o + orow + dh0) = w;
-        } else {
-          u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-          *(u32x2*)((uint16_t*)a.o + orow + dh0) = w;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dh0 = 32 * db + 8 * g + 4 * hh;
+          const float o0 = oacc[qb2][db][4 * g + 0] * inv, o1 = oacc[qb2][db][4 * g + 1] * inv;
+          const float o2 = oacc[qb2][db][4 * g + 2] * inv, o3 = oacc[qb2][db][4 * g + 3] * inv;
+          if (a.o_f32) {
+            f32x4 w = {o0, o1, o2, o3};
+            *(f32x4*)((float*)a.o + orow + dh0) = w;
+          } else {
+            u32x2 w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+            *(u32x2*)((uint16_t*)a.o + orow + dh0) = w;
+          }
         }
-      }
-    if (hh == 0) a.lse[(size_t)bh * T + i] = (m + __log2f(lt)) * kLn2;
+      if (hh == 0) a.lse[(size_t)bh * T + i] = (m[qb2] + __log2f(lt)) * kLn2;
+    }
   }
 }
 
@@ -342,9 +472,11 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a, int nqb) {
 
 template <int DH, bool CAUSAL>
 hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.T + kMQ - 1) / kMQ;
+  constexpr int NQB = DH <= 64 ? 2 : 1;
+  constexpr int MQ = 4 * 32 * NQB;
+  const int nqb = (a.T + MQ - 1) / MQ;
   const long nblocks = (long)nqb * a.B * a.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, nqb);
+  hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL, NQB>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, nqb);
   return hipGetLastError();
 }
 

@@ -12,19 +12,31 @@
 
 namespace bam {
 
+// Entry t of head h holds distance d = d_first + step * t.  Distances outside
+// [dlo, dhi] are padding: -inf in the bias table (a key never visible), 0 in the
+// derivative tables.
 __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restrict__ alpha,
                                                           const float* __restrict__ beta,
-                                                          const float* __restrict__ mu, int d0, int n,
-                                                          int stride, float scale, float* __restrict__ tab,
+                                                          const float* __restrict__ mu, int d_first,
+                                                          int step, int n, int stride, int dlo, int dhi,
+                                                          float scale, float* __restrict__ tab,
                                                           float* __restrict__ ta,
                                                           float* __restrict__ tb) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
   if (t >= n) return;
+  const int d = d_first + step * t;
+  const size_t idx = (size_t)h * stride + t;
+  if (d < dlo || d > dhi) {
+    tab[idx] = -__builtin_huge_valf();
+    if (ta) ta[idx] = 0.f;
+    if (tb) tb[idx] = 0.f;
+    return;
+  }
   const double a = alpha[h];
   const double be = beta[h];
   const double m = mu ? (double)mu[h] : 0.0;
-  const double x = (double)(d0 + t) - m;
+  const double x = (double)d - m;
   const double u = __builtin_isinf(a) ? 0.0 : fabs(x) / a;
   double b, da = 0.0, db = 0.0;
   if (be == 0.0) {
@@ -38,7 +50,6 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
     da = be * p / a;
     db = -p * log(u);
   }
-  const size_t idx = (size_t)h * stride + t;
   tab[idx] = (float)(b * scale);
   if (ta) ta[idx] = (float)da;
   if (tb) tb[idx] = (float)db;
@@ -47,9 +58,16 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
 hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
                               int n, int stride, float scale, float* tab, float* dalpha, float* dbeta,
                               hipStream_t stream) {
+  return launch_prior_table_ex(alpha, beta, mu, H, d0, 1, n, stride, d0, d0 + n - 1, scale, tab, dalpha,
+                               dbeta, stream);
+}
+
+hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, int H, int d_first,
+                                 int step, int n, int stride, int dlo, int dhi, float scale, float* tab,
+                                 float* dalpha, float* dbeta, hipStream_t stream) {
   dim3 grid((n + 255) / 256, H);
-  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), 0, stream, alpha, beta, mu, d0, n, stride, scale,
-                     tab, dalpha, dbeta);
+  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), 0, stream, alpha, beta, mu, d_first, step, n,
+                     stride, dlo, dhi, scale, tab, dalpha, dbeta);
   return hipGetLastError();
 }
 
