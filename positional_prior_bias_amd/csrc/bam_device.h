@@ -41,6 +41,31 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
+
+// two floats -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo + hi of a packed fp16 pair (v_dot2_f32_f16 against (1, 1), fp32 accumulate)
+__device__ __forceinline__ float sum_f16x2(uint32_t packed, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
+}
+
+// a packed bf16 pair -> the same two values as a packed fp16 pair (exact for magnitudes
+// in [2^-14, 65504]; below that fp16 keeps fewer bits, above it the value overflows)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Per-head SSMax factor c = s ln(n) (natural log); 1 with SSMax off.
@@ -57,6 +82,17 @@ __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+
+// Scheduling hint for the basic block it closes: `lead` VALU ops, then NMFMA times one MFMA
+// followed by `per` VALU ops (masks: 0x2 VALU, 0x8 MFMA).
+#define BAM_INTERLEAVE(NMFMA, lead, per)                            \
+  do {                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x002, (lead), 0);         \
+    _Pragma("unroll") for (int bam_i_ = 0; bam_i_ < (NMFMA); ++bam_i_) { \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            \
+      __builtin_amdgcn_sched_group_barrier(0x002, (per), 0);        \
+    }                                                               \
+  } while (0)
 
 }  // namespace bam
 
@@ -120,5 +156,85 @@ __device__ __forceinline__ bf16x8 read_T_operand(const uint16_t* tileT, int row,
   const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
   return as_bf16x8(av);
 }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define BAM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Buffer resource for raw (unswizzled) buffer loads of `bytes` bytes from `base`; every
+// field is made wave-uniform.  Loads whose VGPR offset is at or beyond `bytes` return zeros.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct buffer -> LDS loads (lane l writes lds_base + size * l), written as inline
+// assembly so the compiler does not track them: its own tracking of such loads makes every
+// later LDS read wait for all of them, which would drain the prefetch of later tiles.  The
+// caller orders them with BAM_WAIT_VMCNT / BAM_BARRIER_VMCNT (each load counts once).
+// `soff` and `lds_base` must be wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t voff, uint32_t soff, void* lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(lds_addr(lds_base))
+               : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t voff, uint32_t soff, void* lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(lds_addr(lds_base))
+               : "memory");
+}
+
+// Transposing LDS read (gfx950): in each group of 16 lanes, lane i receives element i of
+// the 4-element rows read by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Row swizzle of the 16-byte chunks of a 128-byte (Dh = 64) row in LDS: with m = row / 2,
+// s = m ^ ((m & 1) << 2).  The 16 rows read by 16 lanes of a K operand read then hit 16
+// distinct chunk slots of the 256-byte bank space, and the 4 rows x 4 chunks of each half
+// wave of a transposing V read do too.  Other head sizes use the Gray code of the row.
+template <int DH>
+__device__ __forceinline__ int vswz(int r) {
+  if (DH == 64) {
+    const int mm = r >> 1;
+    return (mm ^ ((mm & 1) << 2)) & 7;
+  }
+  return swz_chunk(r, DH / 8 - 1);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt / lgkmcnt left at max)
+#define BAM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Work-group barrier that waits only for this wave's LDS operations and for all but the
+// newest `n` of its vector-memory operations (direct-to-LDS loads still in flight for
+// later tiles).  __syncthreads() would drain every outstanding load at each barrier.
+// The empty asm statements keep the compiler from moving memory operations across it.
+#define BAM_BARRIER_VMCNT(n)                                                          \
+  do {                                                                                \
+    asm volatile("" ::: "memory");                                                    \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (0 << 8)); \
+    __builtin_amdgcn_s_barrier();                                                     \
+    asm volatile("" ::: "memory");                                                    \
+  } while (0)
+
+// Scheduling hint for the basic block it closes: `lead` VALU ops, then NMFMA times one MFMA
+// followed by `per` VALU ops (masks: 0x2 VALU, 0x8 MFMA).
+#define BAM_INTERLEAVE(NMFMA, lead, per)                            \
+  do {                                                              \
+    __builtin_amdgcn_sched_group_barrier(0x002, (lead), 0);         \
+    _Pragma("unroll") for (int bam_i_ = 0; bam_i_ < (NMFMA); ++bam_i_) { \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            \
+      __builtin_amdgcn_sched_group_barrier(0x002, (per), 0);        \
+    }                                                               \
+  } while (0)
 
 }  // namespace bam

@@ -20,7 +20,7 @@ hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const fl
 // Forward distance table: reversed (entry u holds d = dhi + kFwdTabPad - u), padded by
 // kFwdTabPad entries of -inf on both sides and scaled by sqrt(Dh), so every per-tile
 // window of the forward kernel is one contiguous, in-bounds copy.
-constexpr int kFwdTabPad = 320;
+constexpr int kFwdTabPad = 704;
 
 struct FwdArgs {
   const void* q;

@@ -6,27 +6,30 @@
 // Flash-style: one pass over key tiles with an online softmax in the exp2 domain;
 // the exact result of the dense definition up to float rounding.
 //
-// bf16 kernel design (wave64, v_mfma_f32_32x32x16_bf16):
+// bf16 kernel design (wave64):
 //   * A work-group of 4 waves owns 256 query rows of one (b, h) (128 for Dh = 128); each
 //     wave owns 64 rows as two 32-row blocks that share every K and V^T operand read.
-//   * Key tiles of 64 are double-buffered in LDS: the next tile is loaded from HBM into
-//     registers while the current one is computed, then stored; one barrier per tile.
-//   * S^T = K Q^T is computed with keys as MFMA rows and queries as columns, so each
-//     lane owns one query (column) and 16 keys per 32x32 block; the row max / sum of
-//     the softmax is an in-lane reduction plus one exchange with lane ^ 32.
-//   * The bias enters as the MFMA accumulator's initial value: the accumulator is
-//     loaded with sqrt(Dh) * b(i - j) from a window of the per-head distance table
-//     staged in LDS (stored in reverse distance order, so a lane's 16 values are read
-//     in register order), and the MFMA returns q.k + sqrt(Dh) b directly.  Distances
-//     the causal mask forbids hold -inf in that window, so masking is free as well.
-//   * The running max is rescaled lazily: O and l are rescaled only when a row max
-//     grows by more than 2^8, otherwise the old max is kept (p <= 2^8 is exact enough
-//     in fp32 accumulators and bf16 P).
-//   * O^T = V^T P^T: P^T is fed from the S^T accumulators without any lane exchange
-//     by letting the MFMA's contraction index run over the keys in the order the
-//     accumulator holds them; V is staged transposed in LDS to match.
-//   * K tiles are staged in LDS with 16-byte chunks XOR-swizzled by row (Gray code)
-//     so the 16-byte operand reads of 32 rows do not collide in banks.
+//   * Key tiles of 64 go straight from HBM to LDS (buffer loads to LDS, issued from inline
+//     assembly so the compiler does not make every LDS read wait for them), three tiles in
+//     flight, one barrier per tile; rows at or beyond T load as zeros.
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) with keys as MFMA rows and queries as
+//     columns: each lane owns one query and 16 keys per 32x32 block, so the row max / sum
+//     of the softmax is an in-lane reduction plus one exchange with lane ^ 32.
+//   * The bias enters as the MFMA accumulator's initial value: the accumulator is loaded
+//     with sqrt(Dh) * b(i - j) from a window of the per-head distance table staged in LDS
+//     (stored in reverse distance order, so a lane's values are read in register order),
+//     and the MFMA returns q.k + sqrt(Dh) b directly.  Distances the causal mask forbids
+//     hold -inf in that window, so masking is free as well.
+//   * The running max is rescaled lazily: O and l are rescaled only when a row max grows
+//     by more than 2^8.
+//   * O^T = V^T P^T with P and V in fp16 (v_mfma_f32_32x32x16_f16): P^T is fed from the
+//     S^T accumulators without any lane exchange (the contraction index runs over the keys
+//     in the order the accumulator holds them); V^T comes from transposing LDS reads of the
+//     row-major tile, which each wave converts from bf16 to fp16 for the chunks it loaded.
+//     l sums the same fp16-rounded weights, so O / l is a convex combination of V rows and
+//     lse is within 2^-11 of the fp32 value.
+//   * K / V rows in LDS have their 16-byte chunks XOR-swizzled by row so operand reads do
+//     not collide in banks.
 #include <float.h>
 
 #include "bam_device.h"
@@ -37,36 +40,6 @@ namespace bam {
 namespace {
 
 constexpr int kNK = 64;    // keys per tile
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define BAM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// Direct HBM -> LDS copies (no VGPR staging): lane l writes lds_base + size * l.
-__device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, BAM_LDS(lds_base), 16, 0, 0);
-}
-__device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, BAM_LDS(lds_base), 4, 0, 0);
-}
-
-// Transposing LDS read (gfx950): in each group of 16 lanes, lane i receives element i of
-// the 4-element rows read by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4.
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-}
-
-// Row swizzle of the 16-byte chunks of a 128-byte (Dh = 64) row in LDS: with m = row / 2,
-// s = m ^ ((m & 1) << 2).  The 16 rows read by 16 lanes of a K operand read then hit 16
-// distinct chunk slots of the 256-byte bank space, and the 4 rows x 4 chunks of each half
-// wave of a transposing V read do too.  Other head sizes use the Gray code of the row.
-template <int DH>
-__device__ __forceinline__ int vswz(int r) {
-  if (DH == 64) {
-    const int mm = r >> 1;
-    return (mm ^ ((mm & 1) << 2)) & 7;
-  }
-  return swz_chunk(r, DH / 8 - 1);
-}
 
 // Four copies of the reversed distance window, copy c shifted by c entries, so every lane
 // reads its runs of 4 consecutive distances with one aligned 16-byte load.  Copies are
@@ -80,8 +53,6 @@ struct FwdTile {
   float w[4][TW + 16];
 };
 
-// s_waitcnt with only the vector-memory counter constrained (expcnt / lgkmcnt left at max)
-#define BAM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
@@ -117,7 +88,7 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31;
   const int hh = lane >> 5;
   const int i0 = qb * MQ;
@@ -125,7 +96,7 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
 
   // Q^T operands: lane holds q_i[16 ks + 8 hh .. + 7] of its query in each block
   bf16x8 qf[NQB][KS];
-  float Cl[NQB], m[NQB], l[NQB], lr[NQB];
+  float Cl[NQB], m[NQB], l[NQB];
   const float sqrtD = __builtin_sqrtf((float)DH);
   const float sh = a.ssmax ? a.s[h] : 1.0f;
 #pragma unroll
@@ -142,7 +113,6 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
     Cl[qb2] = fmaxf(c * kLog2e / sqrtD, FLT_MIN);
     m[qb2] = kNegInf;
     l[qb2] = 0.f;
-    lr[qb2] = 0.f;
   }
   f32x16 oacc[NQB][DB];
 #pragma unroll
@@ -154,7 +124,7 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
 
   const int kend = CAUSAL ? min(T, i0 + MQ) : T;
   const int ntiles = (kend + kNK - 1) / kNK;
-  const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
+  const float* tabh = a.tab + (size_t)h * a.tab_stride;
 
   // window value index y of this lane's first accumulator group; the four values of each
   // group are consecutive, read with one 16-byte load from copy (y & 3)
@@ -162,31 +132,79 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   const int wcopy = ybase & 3;
 
   // ---- issue the direct loads of key tile j0.  Chunk position p of K / V holds global
-  // chunk (row, (p % KCH) ^ swizzle(row)); rows past T are clamped to T - 1 (in bounds;
-  // those keys are masked by the table or explicitly).  Every wave issues LPT loads.
+  // chunk (row, (p % KCH) ^ swizzle(row)).  Buffer loads: the per-lane part of each address
+  // is a fixed VGPR offset; rows at or beyond T lie outside the K / V buffer ranges and load
+  // as zeros (those keys are masked by the table or explicitly).  Every wave issues LPT loads.
+  const i32x4 rK = buffer_rsrc(K, (uint32_t)T * DH * 2);
+  const i32x4 rV = buffer_rsrc(V, (uint32_t)T * DH * 2);
+  const i32x4 rW = buffer_rsrc(tabh, (uint32_t)a.tab_stride * 4);
+  int kv_voff[CPW];
+#pragma unroll
+  for (int r = 0; r < CPW; ++r) {
+    const int p = (wave * CPW + r) * 64 + lane;
+    const int row = p / KCH;
+    kv_voff[r] = (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
+  }
   auto issue_tile = [&](FwdTile<DH, TW>& tl, int j0) {
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       const int p0 = (wave * CPW + r) * 64;
-      const int p = p0 + lane;
-      const int row = p / KCH;
-      const int gc = (p % KCH) ^ vswz<DH>(row);
-      const size_t off = (size_t)min(j0 + row, T - 1) * DH + gc * 8;
-      g2lds16(K + off, &tl.k[p0 * 8]);
-      g2lds16(V + off, &tl.v[p0 * 8]);
+      lds_dma16(rK, kv_voff[r] + j0 * DH * 2, 0, &tl.k[p0 * 8]);
+      lds_dma16(rV, kv_voff[r] + j0 * DH * 2, 0, &tl.v[p0 * 8]);
     }
     const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
 #pragma unroll
     for (int r = 0; r < WPW; ++r) {
       const int x = wave * WPW + r;         // 0 .. 4 * TW / 64 - 1
       const int cpy = x / (TW / 64), seg = x % (TW / 64);
-      g2lds4(tabh + u0 + cpy + 64 * seg + lane, &tl.w[cpy][64 * seg]);
+      lds_dma4(rW, lane * 4, (u0 + cpy + 64 * seg) * 4, &tl.w[cpy][64 * seg]);
     }
   };
 
-  auto compute_tile = [&](const FwdTile<DH, TW>& tl, int j0) {
+  // Dh = 64: per-lane LDS byte offsets of the K and V^T operand reads, fixed for the whole
+  // kernel.  V^T operand rows r0 = 16 st + rb and r1 = r0 + 8, column 32 db + cq: the row
+  // swizzle of rb + 16 st does not depend on st and that of r1 is that of r0 with bit 2
+  // flipped, so the four (db, r0 / r1) combinations use two offsets, vA and vB, plus
+  // immediates.  K operand row 32 kb + ql: the swizzle does not depend on kb.
+  int vA = 0, vB = 0, kOff[KS];
+  if constexpr (DH == 64) {
+    const int G = lane >> 4, gi = lane & 15;
+    const int rb = 4 * (G >> 1) + (gi >> 2);
+    const int ch0 = (2 * (G & 1) + ((gi & 3) >> 1)) ^ vswz<DH>(rb);
+    vA = 128 * rb + 16 * ch0 + 8 * (gi & 1);
+    vB = 128 * rb + 16 * (ch0 ^ 4) + 8 * (gi & 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kOff[ks] = 128 * ql + 16 * ((2 * ks + hh) ^ vswz<DH>(ql));
+  }
+
+  // ---- V is converted from bf16 to fp16 in LDS once per tile, each wave converting the
+  // chunks its own direct loads wrote (so it only waits for its own loads), before the
+  // barrier that publishes the tile.  P is rounded to fp16 for the PV product.
+  auto convert_v = [&](FwdTile<DH, TW>& tl) {
+#pragma unroll
+    for (int r = 0; r < CPW; ++r) {
+      u32x4* pv = (u32x4*)&tl.v[((wave * CPW + r) * 64 + lane) * 8];
+      const u32x4 w = *pv;
+      const u32x4 hw = {bf16x2_to_f16x2(w[0]), bf16x2_to_f16x2(w[1]), bf16x2_to_f16x2(w[2]),
+                        bf16x2_to_f16x2(w[3])};
+      *pv = hw;
+    }
+  };
+  // wait for this wave's loads of tile t + 1 (tile t + 2's may stay in flight), convert it
+  auto convert_next = [&](FwdTile<DH, TW>& nx, int t) {
+    if (t + 1 >= ntiles) return;
+    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
+    else BAM_WAIT_VMCNT(0);
+    convert_v(nx);
+  };
+
+  auto compute_tile = [&](const FwdTile<DH, TW>& tl, FwdTile<DH, TW>& nx, int t) {
+    const int j0 = t * kNK;
     // a wave whose rows all precede this tile's keys has nothing to do (causal)
-    if (CAUSAL && j0 > iw + QW - 1) return;
+    if (CAUSAL && j0 > iw + QW - 1) {
+      convert_next(nx, t);
+      return;
+    }
     // ---- S'^T = K Q^T + sqrt(Dh) b: each accumulator starts from its bias block (read
     // straight into the accumulator registers), then accumulates the contraction.  All
     // LDS reads of the phase are issued before the first MFMA so their latency overlaps.
@@ -207,10 +225,16 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
           sacc[qb2][kb][4 * g + 3] = v4[3];
         }
       }
-      const int r = 32 * kb + ql;
+      if constexpr (DH == 64) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kw[kb][ks] = *(const u32x4*)(&tl.k[r * DH + ((2 * ks + hh) ^ vswz<DH>(r)) * 8]);
+        for (int ks = 0; ks < KS; ++ks)
+          kw[kb][ks] = *(const u32x4*)((const char*)tl.k + kOff[ks] + 4096 * kb);
+      } else {
+        const int r = 32 * kb + ql;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kw[kb][ks] = *(const u32x4*)(&tl.k[r * DH + ((2 * ks + hh) ^ vswz<DH>(r)) * 8]);
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -235,45 +259,48 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
     u32x4 pf[NQB][4];
 #pragma unroll
     for (int qb2 = 0; qb2 < NQB; ++qb2) {
-      float mx = kNegInf;
+      float mxa = kNegInf, mxb = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; x += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[qb2][kb][x], sacc[qb2][kb][x + 1]));
-      mx = max_xor32(mx);
+        for (int x = 0; x < 16; x += 4) {
+          mxa = __builtin_fmaxf(mxa, __builtin_fmaxf(sacc[qb2][kb][x], sacc[qb2][kb][x + 1]));
+          mxb = __builtin_fmaxf(mxb, __builtin_fmaxf(sacc[qb2][kb][x + 2], sacc[qb2][kb][x + 3]));
+        }
+      const float mx = max_xor32(__builtin_fmaxf(mxa, mxb));
       const float cand = Cl[qb2] * mx;
       if (__any(cand > m[qb2] + kLazy)) {
         const float m_new = fmaxf(m[qb2], cand);
         const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(m[qb2] - m_new);
         m[qb2] = m_new;
         l[qb2] *= sc;
-        lr[qb2] *= sc;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int x = 0; x < 16; ++x) oacc[qb2][db][x] *= sc;
       }
       const float m_use = (m[qb2] == kNegInf) ? 0.f : m[qb2];
-      // lr sums the same bf16-rounded weights the PV product uses (v_dot2 with (1, 1)):
-      // O is normalised by it, an exact convex combination of the rows of V under those
-      // weights.  l sums the fp32 weights and gives lse.
-      float ls[2] = {0.f, 0.f}, le[2] = {0.f, 0.f};
+      // l sums the same fp16-rounded weights the PV product uses (v_dot2 with (1, 1)): O is
+      // normalised by it, an exact convex combination of the rows of V under those weights,
+      // and lse comes from it too (each weight is within 2^-11 of its fp32 value).
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; x += 2) {
           const float p0 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x], -m_use));
           const float p1 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x + 1], -m_use));
-          const uint32_t pk = pack_bf16x2(p0, p1);
+          const uint32_t pk = pack_f16x2(p0, p1);
           pf[qb2][2 * kb + (x >> 3)][(x & 7) >> 1] = pk;
-          ls[(x >> 1) & 1] = sum_bf16x2(pk, ls[(x >> 1) & 1]);
-          le[(x >> 1) & 1] += p0 + p1;
+          ls[(x >> 1) & 1] = sum_f16x2(pk, ls[(x >> 1) & 1]);
         }
-      lr[qb2] += ls[0] + ls[1];
-      l[qb2] += le[0] + le[1];
+      l[qb2] += ls[0] + ls[1];
     }
 
-    // ---- O^T += V^T P^T.  The V^T operand of lane (dh, hh) holds keys
+    // the next tile's V is converted here, between the softmax and the PV product
+    convert_next(nx, t);
+
+    // ---- O^T += V^T P^T (fp16).  The V^T operand of lane (dh, hh) holds keys
     // {16 st + 4 hh + 0..3, + 8 .. + 11} of column dh: two transposing reads of the
     // row-major V tile (lane i of 16-lane group G reads row key0 + i / 4, columns
     // dh0 + 4 (i % 4) .. + 3, dh0 = 32 db + 16 (G % 2)).
@@ -281,52 +308,59 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int col = 32 * db + 16 * (G & 1) + 4 * (gi & 3);
-      bf16x8 av[4];
+      f16x8 av[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int r0 = 16 * st + 4 * (G >> 1) + (gi >> 2);
-        const int r1 = r0 + 8;
-        const s16x4 v0 = lds_read_tr16(&tl.v[r0 * DH + (((col >> 3) ^ vswz<DH>(r0)) << 3) + (col & 7)]);
-        const s16x4 v1 = lds_read_tr16(&tl.v[r1 * DH + (((col >> 3) ^ vswz<DH>(r1)) << 3) + (col & 7)]);
+        s16x4 v0, v1;
+        if constexpr (DH == 64) {
+          const char* tv = (const char*)tl.v;
+          v0 = lds_read_tr16((const uint16_t*)(tv + (db ? vB : vA) + 2048 * st));
+          v1 = lds_read_tr16((const uint16_t*)(tv + (db ? vA : vB) + 2048 * st + 1024));
+        } else {
+          const int r0 = 16 * st + 4 * (G >> 1) + (gi >> 2);
+          const int r1 = r0 + 8;
+          v0 = lds_read_tr16(&tl.v[r0 * DH + (((col >> 3) ^ vswz<DH>(r0)) << 3) + (col & 7)]);
+          v1 = lds_read_tr16(&tl.v[r1 * DH + (((col >> 3) ^ vswz<DH>(r1)) << 3) + (col & 7)]);
+        }
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        av[st] = __builtin_bit_cast(bf16x8, vv);
+        av[st] = __builtin_bit_cast(f16x8, vv);
       }
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int qb2 = 0; qb2 < NQB; ++qb2)
-          oacc[qb2][db] = mfma32x32x16(av[st], as_bf16x8(pf[qb2][st]), oacc[qb2][db]);
+          oacc[qb2][db] = mfma32x32x16_f16(av[st], as_f16x8(pf[qb2][st]), oacc[qb2][db]);
     }
   };
 
-  // ---- three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load
+  // ---- three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load.  Q is
+  // in registers before the first tile load is issued (the compiler would otherwise wait
+  // for it, and so for every load in flight, inside the loop).
+  BAM_WAIT_VMCNT(0);
   issue_tile(tA, 0);
   if (ntiles > 1) {
     issue_tile(tB, kNK);
-    BAM_WAIT_VMCNT(LPT);    // tile 0 landed (tile 1 may still be in flight)
+    BAM_WAIT_VMCNT(LPT);       // this wave's loads of tile 0 landed (tile 1 may be in flight)
   } else {
     BAM_WAIT_VMCNT(0);
   }
-  __syncthreads();
-  // wait for tile t + 1 (tile t + 2 may still be in flight) and publish it
-  auto advance = [&](int t) {
-    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
-    else BAM_WAIT_VMCNT(0);
-    __syncthreads();
-  };
+  convert_v(tA);
+  BAM_BARRIER_VMCNT(63);       // publish tile 0
+  // every wave has waited for its loads of tile t + 1 (in compute_tile); publish it
+  auto advance = [&]() { BAM_BARRIER_VMCNT(63); };
   for (int t = 0; t < ntiles; t += 3) {
     if (t + 2 < ntiles) issue_tile(tC, (t + 2) * kNK);
-    compute_tile(tA, t * kNK);
-    advance(t);
+    compute_tile(tA, tB, t);
+    advance();
     if (t + 1 >= ntiles) break;
     if (t + 3 < ntiles) issue_tile(tA, (t + 3) * kNK);
-    compute_tile(tB, (t + 1) * kNK);
-    advance(t + 1);
+    compute_tile(tB, tC, t + 1);
+    advance();
     if (t + 2 >= ntiles) break;
     if (t + 4 < ntiles) issue_tile(tB, (t + 4) * kNK);
-    compute_tile(tC, (t + 2) * kNK);
-    advance(t + 2);
+    compute_tile(tC, tA, t + 2);
+    advance();
   }
 
   // ---- epilogue
@@ -334,9 +368,8 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   for (int qb2 = 0; qb2 < NQB; ++qb2) {
     const int i = iw + 32 * qb2 + ql;
     const float lt = l[qb2] + xor32(l[qb2]);
-    const float lrt = lr[qb2] + xor32(lr[qb2]);
     if (i < T) {
-      const float inv = 1.0f / lrt;
+      const float inv = 1.0f / lt;
       const size_t orow = base + (size_t)i * DH;
 #pragma unroll
       for (int db = 0; db < DB; ++db)

@@ -45,11 +45,11 @@ def test_status_strings(L):
 
 
 def test_workspace_sizes(L):
-    # distance table only: H rows of T (causal) or 2T-1 distances, padded by 320 entries on
+    # distance table only: H rows of T (causal) or 2T-1 distances, padded by 704 entries on
     # each side, rounded up to 64 entries; 256-byte aligned
     pad64 = lambda n: (n + 63) // 64 * 64  # noqa: E731
-    assert L.bam_fwd_workspace_size(32, 12, 512, 64, 3) == 12 * pad64(512 + 640) * 4
-    assert L.bam_fwd_workspace_size(1, 4, 256, 32, 0) == 4 * pad64(511 + 640) * 4
+    assert L.bam_fwd_workspace_size(32, 12, 512, 64, 3) == 12 * pad64(512 + 2 * 704) * 4
+    assert L.bam_fwd_workspace_size(1, 4, 256, 32, 0) == 4 * pad64(511 + 2 * 704) * 4
     assert L.bam_fwd_workspace_size(1, 0, 256, 32, 1) == 0
     assert L.bam_decode_workspace_size(8, 12, 256000, 64) > 12 * 256000 * 4
     assert L.bam_decode_workspace_size(8, 12, 256000, 48) == 0

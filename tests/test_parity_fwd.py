@@ -84,12 +84,18 @@ CASES = [
     (300, 64, False, True, (0.2, 1.2), 0.0),
     (513, 32, True, True, (0.2, 1.2), 0.0),
     (700, 128, False, False, (0.5, 2.0), 0.0),
+    # long sequences (the 512-row ping-pong kernel serves Dh = 64 from T = 2048 on)
+    (2048, 64, True, True, (0.1, 0.9), 0.0),
+    (2100, 64, True, True, (-0.8, -0.1), -0.5),
+    (2333, 64, False, True, (0.2, 1.2), 0.0),
+    (4097, 64, True, False, (0.3, 1.5), 0.0),
 ]
 
 
 @pytest.mark.parametrize("T,Dh,causal,ssmax,br,mu", CASES)
 def test_bf16_random(T, Dh, causal, ssmax, br, mu):
-    w = wl.random_case(100 + T + Dh, 2, 3, T, Dh, "bf16", wl.CAUSAL * causal | wl.SSMAX * ssmax, beta_range=br,
+    B = 2 if T < 2048 else 1
+    w = wl.random_case(100 + T + Dh, B, 3, T, Dh, "bf16", wl.CAUSAL * causal | wl.SSMAX * ssmax, beta_range=br,
                        mu=mu)
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=causal, ssmax=ssmax)
