@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a, long nrows) {
 
 // ------------------------------------------------------------------------------------
 template <int DH, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a, int nkb) {
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
   constexpr int TW = kQT + kKB;   // distance window
