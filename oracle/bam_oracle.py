@@ -23,6 +23,13 @@ softmax, no split-KV, no distance table):
   beta = 0 gives -1 (0^0 = 1); alpha = +inf gives u = 0; u = 0 with beta < 0 is a
   precondition violation and raises.
 * lse is the natural-log log-sum-exp of the logits of a row.
+* Reference parameterisation (Bayesian Attention Mechanism README, "Implementation
+  Details", the formula and the AttentionPrior code): b = -e^theta_alpha *
+  (|(j - i) - mu| + eps)^theta_beta with mu = e^theta_mu - e^-theta_mu and eps = 1e-5.
+  The printed formula writes (i - j) - mu while the code subtracts mu from
+  positions[j] - positions[i]; the two agree for mu = 0 (the default, theta_mu = 0)
+  and the code's sign is adopted here.  param="ref" selects it; the alpha / beta / mu
+  arrays then hold theta_alpha / theta_beta / theta_mu.
 
 Pins (tests/test_oracle_pins.py) tie this module to things other than itself:
 the printed ALiBi worked example, torch's scaled_dot_product_attention on the
@@ -38,7 +45,9 @@ import math
 import numpy as np
 
 __all__ = [
-    "prior_bias", "prior_bias_dalpha", "prior_bias_dbeta", "ssmax_factor",
+    "prior_bias", "prior_bias_dalpha", "prior_bias_dbeta", "prior_bias_dmu", "ssmax_factor",
+    "REF_EPS", "ref_mu", "prior_bias_ref", "prior_bias_ref_dtheta_alpha", "prior_bias_ref_dtheta_beta",
+    "prior_bias_ref_dtheta_mu",
     "attn_fwd", "attn_fwd_rows", "attn_decode", "attn_bwd", "attention_probs",
 ]
 
@@ -106,6 +115,82 @@ def prior_bias_dbeta(d, alpha, beta, mu=0.0):
     return out
 
 
+def prior_bias_dmu(d, alpha, beta, mu=0.0):
+    """db/dmu = beta * u^beta / x with x = d - mu (0 where u = 0, beta = 0 or alpha = inf).
+
+    The derivative of -(|x| / alpha)^beta in x is -beta u^beta / x and dx/dmu = -1.  At
+    x = 0 the sign of x is taken as 0 (so the term is 0 even where the cusp of
+    0 < beta < 1 makes the one-sided derivatives infinite).
+    """
+    x = np.asarray(d, np.float64) - float(mu)
+    u = _u(d, alpha, mu)
+    beta = float(beta)
+    out = np.zeros_like(u)
+    if beta == 0.0 or math.isinf(float(alpha)):
+        return out
+    nz = u != 0.0
+    if beta < 0.0 and not np.all(nz):
+        raise PreconditionError("bias undefined: u = 0 with beta < 0")
+    out[nz] = beta * np.power(u[nz], beta) / x[nz]
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Reference parameterisation (Bayesian Attention Mechanism README, "Implementation
+# Details"): -e^theta_alpha (|(j - i) - mu| + eps)^theta_beta, mu = e^theta_mu - e^-theta_mu
+# --------------------------------------------------------------------------------------
+
+REF_EPS = 1e-5
+
+
+def ref_mu(theta_mu):
+    """mu = e^theta_mu - e^-theta_mu."""
+    t = float(theta_mu)
+    return math.exp(t) - math.exp(-t)
+
+
+def _ref_x(d, theta_mu):
+    """x = (j - i) - mu for a distance d = i - j."""
+    return -np.asarray(d, np.float64) - ref_mu(theta_mu)
+
+
+def prior_bias_ref(d, theta_alpha, theta_beta, theta_mu=0.0, eps=REF_EPS):
+    """b(d) = -e^theta_alpha * (|x| + eps)^theta_beta, x = (j - i) - mu, for d = i - j."""
+    g = np.abs(_ref_x(d, theta_mu)) + float(eps)
+    return -math.exp(float(theta_alpha)) * np.power(g, float(theta_beta))
+
+
+def prior_bias_ref_dtheta_alpha(d, theta_alpha, theta_beta, theta_mu=0.0, eps=REF_EPS):
+    """db/dtheta_alpha = b."""
+    return prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps)
+
+
+def prior_bias_ref_dtheta_beta(d, theta_alpha, theta_beta, theta_mu=0.0, eps=REF_EPS):
+    """db/dtheta_beta = b * ln(|x| + eps)."""
+    g = np.abs(_ref_x(d, theta_mu)) + float(eps)
+    return prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps) * np.log(g)
+
+
+def prior_bias_ref_dtheta_mu(d, theta_alpha, theta_beta, theta_mu=0.0, eps=REF_EPS):
+    """db/dtheta_mu = (db/dmu)(dmu/dtheta_mu): db/dmu = -b theta_beta sign(x) / (|x| + eps)
+    (sign(0) = 0) and dmu/dtheta_mu = e^theta_mu + e^-theta_mu."""
+    x = _ref_x(d, theta_mu)
+    g = np.abs(x) + float(eps)
+    b = prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps)
+    t = float(theta_mu)
+    return -b * float(theta_beta) * np.sign(x) / g * (math.exp(t) + math.exp(-t))
+
+
+def _bias_fns(param):
+    """(bias, d/dp1, d/dp2, d/dp3) of a parameterisation, each f(d, p1, p2, p3)."""
+    if param == "alpha":
+        return prior_bias, prior_bias_dalpha, prior_bias_dbeta, prior_bias_dmu
+    if param == "ref":
+        return (prior_bias_ref, prior_bias_ref_dtheta_alpha, prior_bias_ref_dtheta_beta,
+                prior_bias_ref_dtheta_mu)
+    raise ValueError(f"unknown parameterisation {param!r}")
+
+
 def ssmax_factor(n, s, ssmax: bool):
     """c = s * ln(n) with Scalable-Softmax on, the literal 1 with it off.
 
@@ -122,7 +207,7 @@ def ssmax_factor(n, s, ssmax: bool):
 # Forward
 # --------------------------------------------------------------------------------------
 
-def _head_logits(q, k, rows, alpha, beta, mu, s, causal, ssmax, nkeys=None):
+def _head_logits(q, k, rows, alpha, beta, mu, s, causal, ssmax, nkeys=None, param="alpha"):
     """Logits l[r, j] for the query rows `rows` of one head, -inf where not visible.
 
     q: [T, Dh] (or [R, Dh] already sliced when rows is given as positions),
@@ -139,7 +224,7 @@ def _head_logits(q, k, rows, alpha, beta, mu, s, causal, ssmax, nkeys=None):
     c = ssmax_factor(n, s, ssmax)[:, None]
     d = np.broadcast_to(i - j, visible.shape)
     bias = np.full(visible.shape, np.nan)
-    bias[visible] = prior_bias(d[visible], alpha, beta, mu)
+    bias[visible] = _bias_fns(param)[0](d[visible], alpha, beta, mu)
     L = np.full(visible.shape, -np.inf)
     L[visible] = (c * (S + bias))[visible]
     return L, c, S, bias
@@ -152,17 +237,17 @@ def _softmax_rows(L):
     return E / Z, (m + np.log(Z))[:, 0]
 
 
-def attention_probs(q, k, alpha, beta, mu, s, causal=True, ssmax=False, rows=None):
+def attention_probs(q, k, alpha, beta, mu, s, causal=True, ssmax=False, rows=None, param="alpha"):
     """Attention weights P [R, Tk] of one head (q: [T, Dh], k: [Tk, Dh])."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
-    L, _, _, _ = _head_logits(q[rows], k, rows, alpha, beta, mu, s, causal, ssmax)
+    L, _, _, _ = _head_logits(q[rows], k, rows, alpha, beta, mu, s, causal, ssmax, param=param)
     P, _ = _softmax_rows(L)
     return P
 
 
-def attn_fwd_rows(q, k, v, rows, alpha, beta, mu, s, causal=True, ssmax=False, chunk=256):
+def attn_fwd_rows(q, k, v, rows, alpha, beta, mu, s, causal=True, ssmax=False, chunk=256, param="alpha"):
     """O and lse of the query rows `rows` of one head, dense per row block.
 
     q, k, v: [T, Dh] arrays of one (b, h).  Returns O [R, Dh], lse [R] (fp64).
@@ -175,14 +260,14 @@ def attn_fwd_rows(q, k, v, rows, alpha, beta, mu, s, causal=True, ssmax=False, c
     lse = np.empty(rows.size)
     for r0 in range(0, rows.size, chunk):
         rr = rows[r0:r0 + chunk]
-        L, _, _, _ = _head_logits(q[rr], k, rr, alpha, beta, mu, s, causal, ssmax)
+        L, _, _, _ = _head_logits(q[rr], k, rr, alpha, beta, mu, s, causal, ssmax, param=param)
         P, l = _softmax_rows(L)
         O[r0:r0 + chunk] = P @ v
         lse[r0:r0 + chunk] = l
     return O, lse
 
 
-def attn_fwd(q, k, v, alpha, beta, mu, s, causal=True, ssmax=False, heads=None):
+def attn_fwd(q, k, v, alpha, beta, mu, s, causal=True, ssmax=False, heads=None, param="alpha"):
     """Full forward: q, k, v [B, H, T, Dh] -> O [B, H, T, Dh], lse [B, H, T] (fp64).
 
     `heads` optionally restricts the work to a list of (b, h) pairs; other entries
@@ -196,11 +281,11 @@ def attn_fwd(q, k, v, alpha, beta, mu, s, causal=True, ssmax=False, heads=None):
     rows = np.arange(T)
     for b, h in pairs:
         O[b, h], lse[b, h] = attn_fwd_rows(q[b, h], k[b, h], v[b, h], rows,
-                                           alpha[h], beta[h], mu[h], s[h], causal, ssmax)
+                                           alpha[h], beta[h], mu[h], s[h], causal, ssmax, param=param)
     return O, lse
 
 
-def attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax=True, heads=None):
+def attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax=True, heads=None, param="alpha"):
     """One query row per (b, h) against a KV cache.
 
     q [B, H, Dh]; caches [B, H, Lmax, Dh]; kv_len [B].  The cache holds the current
@@ -217,7 +302,7 @@ def attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax=True, hea
         kk = np.asarray(k_cache[b, h, :n], np.float64)
         vv = np.asarray(v_cache[b, h, :n], np.float64)
         L, _, _, _ = _head_logits(qi, kk, np.array([n - 1]), alpha[h], beta[h], mu[h], s[h],
-                                  True, ssmax)
+                                  True, ssmax, param=param)
         P, l = _softmax_rows(L)
         O[b, h] = (P @ vv)[0]
         lse[b, h] = l[0]
@@ -228,17 +313,18 @@ def attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax=True, hea
 # Backward
 # --------------------------------------------------------------------------------------
 
-def attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=True, ssmax=False, heads=None):
+def attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=True, ssmax=False, heads=None, param="alpha"):
     """Gradients of L = sum(O * dO) for every input of the forward.
 
-    Returns a dict with dq, dk, dv [B, H, T, Dh], dalpha, dbeta, ds [H] and the
-    conditioning scales A_alpha, A_beta, A_s [H] (sum of |term| of each parameter
-    sum, used to size tolerances of the cancelling reductions).
+    Returns a dict with dq, dk, dv [B, H, T, Dh], dalpha, dbeta, dmu, ds [H] and the
+    conditioning scales A_alpha, A_beta, A_mu, A_s [H] (sum of |term| of each parameter
+    sum, used to size tolerances of the cancelling reductions).  With param="ref",
+    dalpha / dbeta / dmu are the gradients in theta_alpha / theta_beta / theta_mu.
 
     Chain rule on logit_ij = c_i (S_ij + b_ij), S = q.k / sqrt(Dh):
       dP = dO V^T, D_i = sum_j P_ij dP_ij, dZ = P * (dP - D)  (dZ = dL/dlogit),
       dV = P^T dO, dq_i = c_i sum_j dZ_ij k_j / sqrt(Dh), dk_j = sum_i c_i dZ_ij q_i / sqrt(Dh),
-      dalpha = sum c_i dZ_ij db/dalpha, dbeta = sum c_i dZ_ij db/dbeta,
+      dalpha = sum c_i dZ_ij db/dalpha, dbeta = sum c_i dZ_ij db/dbeta, dmu likewise,
       ds = sum dZ_ij ln(n_i) (S_ij + b_ij)  (SSMax on; 0 otherwise).
     Bayesian Attention Mechanism README, "Implementation Details": alpha's scale
     and beta are the trained per-head parameters.
@@ -249,8 +335,10 @@ def attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=True, ssmax=False, heads=No
     dv = np.full(v.shape, np.nan)
     dalpha = np.zeros(H)
     dbeta = np.zeros(H)
+    dmu = np.zeros(H)
     ds = np.zeros(H)
-    A = np.zeros((3, H))
+    A = np.zeros((4, H))
+    _, f_da, f_db, f_dm = _bias_fns(param)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     rows = np.arange(T)
     for b, h in pairs:
@@ -258,7 +346,8 @@ def attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=True, ssmax=False, heads=No
         kk = np.asarray(k[b, h], np.float64)
         vv = np.asarray(v[b, h], np.float64)
         dd = np.asarray(do[b, h], np.float64)
-        L, c, S, bias = _head_logits(qq, kk, rows, alpha[h], beta[h], mu[h], s[h], causal, ssmax)
+        L, c, S, bias = _head_logits(qq, kk, rows, alpha[h], beta[h], mu[h], s[h], causal, ssmax,
+                                     param=param)
         P, _ = _softmax_rows(L)
         O = P @ vv
         dP = dd @ vv.T
@@ -273,17 +362,20 @@ def attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=True, ssmax=False, heads=No
         j = np.arange(T)[None, :]
         d = np.broadcast_to(i - j, L.shape)[visible]
         cz = (c * dZ)[visible]
-        ta = cz * prior_bias_dalpha(d, alpha[h], beta[h], mu[h])
-        tb = cz * prior_bias_dbeta(d, alpha[h], beta[h], mu[h])
+        ta = cz * f_da(d, alpha[h], beta[h], mu[h])
+        tb = cz * f_db(d, alpha[h], beta[h], mu[h])
+        tm = cz * f_dm(d, alpha[h], beta[h], mu[h])
         dalpha[h] += ta.sum()
         dbeta[h] += tb.sum()
+        dmu[h] += tm.sum()
         A[0, h] += np.abs(ta).sum()
         A[1, h] += np.abs(tb).sum()
+        A[3, h] += np.abs(tm).sum()
         if ssmax:
             n = visible.sum(axis=1).astype(np.float64)[:, None]
             lnn = np.broadcast_to(np.log(n), L.shape)[visible]
             tsum = dZ[visible] * lnn * (S[visible] + bias[visible])
             ds[h] += tsum.sum()
             A[2, h] += np.abs(tsum).sum()
-    return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, ds=ds,
-                A_alpha=A[0], A_beta=A[1], A_s=A[2])
+    return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, dmu=dmu, ds=ds,
+                A_alpha=A[0], A_beta=A[1], A_s=A[2], A_mu=A[3])

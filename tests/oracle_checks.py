@@ -351,28 +351,33 @@ def check_decode(orc):
 # backward
 # ----------------------------------------------------------------------------------
 
-def _loss(orc, q, k, v, do, alpha, beta, mu, s, causal, ssmax):
-    O, _ = orc.attn_fwd(q, k, v, alpha, beta, mu, s, causal=causal, ssmax=ssmax)
+def _loss(orc, q, k, v, do, alpha, beta, mu, s, causal, ssmax, param="alpha"):
+    O, _ = orc.attn_fwd(q, k, v, alpha, beta, mu, s, causal=causal, ssmax=ssmax, param=param)
     return float((O * do).sum())
 
 
-def check_backward_fd(orc):
+def check_backward_fd(orc, param="alpha"):
     rng = np.random.default_rng(18)
     B, H, T, Dh = 1, 3, 6, 4
     q = rng.standard_normal((B, H, T, Dh))
     k = rng.standard_normal((B, H, T, Dh))
     v = rng.standard_normal((B, H, T, Dh))
     do = rng.standard_normal((B, H, T, Dh))
-    alpha = np.array([0.8, 2.5, 3.0])
-    beta = np.array([0.45, 1.3, -0.6])
-    mu = np.array([0.0, 0.0, -0.5])
+    if param == "alpha":
+        alpha = np.array([0.8, 2.5, 3.0])
+        beta = np.array([0.45, 1.3, -0.6])
+        mu = np.array([0.0, 0.3, -0.5])
+    else:   # theta_alpha, theta_beta, theta_mu of the reference form
+        alpha = np.array([0.2, -0.7, 0.5])
+        beta = np.array([0.45, 1.3, -0.6])
+        mu = np.array([0.07, 0.25, -0.4])   # nonzero: no visible pair sits on the kink of |x|
     s = np.array([0.4, 0.6, 0.5])
     eps = 1e-6
     for causal in (True, False):
         for ssmax in (True, False):
-            g = orc.attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=causal, ssmax=ssmax)
-            args = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, s=s)
-            keys = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "s": "ds"}
+            g = orc.attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=causal, ssmax=ssmax, param=param)
+            args = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, mu=mu, s=s)
+            keys = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "mu": "dmu", "s": "ds"}
             for name, gname in keys.items():
                 x = args[name]
                 num = np.zeros_like(x)
@@ -383,13 +388,25 @@ def check_backward_fd(orc):
                     xm[idx] -= eps
                     ap = dict(args, **{name: xp})
                     am = dict(args, **{name: xm})
-                    fp = _loss(orc, ap["q"], ap["k"], ap["v"], do, ap["alpha"], ap["beta"], mu, ap["s"], causal, ssmax)
-                    fm = _loss(orc, am["q"], am["k"], am["v"], do, am["alpha"], am["beta"], mu, am["s"], causal, ssmax)
+                    fp = _loss(orc, ap["q"], ap["k"], ap["v"], do, ap["alpha"], ap["beta"], ap["mu"], ap["s"], causal,
+                               ssmax, param)
+                    fm = _loss(orc, am["q"], am["k"], am["v"], do, am["alpha"], am["beta"], am["mu"], am["s"], causal,
+                               ssmax, param)
                     num[idx] = (fp - fm) / (2 * eps)
                 if name == "s" and not ssmax:
                     num[...] = 0.0
+                got = g[gname]
+                if name == "mu" and param == "alpha":
+                    # head 0 has mu = 0: the cusp of |x|^0.45 at x = 0 makes the central
+                    # difference converge only like h^0.45; compare the other heads
+                    got, num = got[1:], num[1:]
                 scale = max(1.0, np.max(np.abs(num)))
-                _close(g[gname], num, 2e-7 * scale, f"backward FD {gname} causal={causal} ssmax={ssmax}")
+                _close(got, num, 2e-7 * scale, f"backward FD {gname} causal={causal} ssmax={ssmax} {param}")
+
+
+def check_backward_fd_ref(orc):
+    """The same central finite differences for the reference parameterisation (theta's)."""
+    check_backward_fd(orc, param="ref")
 
 
 def check_dalpha_alibi_closed_form(orc):
@@ -415,9 +432,63 @@ def check_special_values(orc):
         raise AssertionError("u = 0 with beta < 0 must raise")
 
 
+# ----------------------------------------------------------------------------------
+# reference parameterisation (Bayesian Attention Mechanism README, "Implementation
+# Details": -e^theta_alpha (|(j - i) - mu| + eps)^theta_beta, mu = e^theta_mu - e^-theta_mu)
+# ----------------------------------------------------------------------------------
+
+def check_ref_mu_is_two_sinh(orc):
+    for t in (-1.3, -0.2, 0.0, 0.05, 0.7, 2.1):
+        _close(orc.ref_mu(t), 2.0 * math.sinh(t), 1e-15 * max(1.0, abs(math.sinh(t))), "mu = 2 sinh(theta_mu)")
+
+
+def check_ref_reduces_to_alpha_form(orc):
+    """With eps = 0 the reference form is the alpha-form: e^theta_alpha = alpha^-beta,
+    theta_beta = beta, and its offset mu = -(alpha-form mu) (it measures j - i)."""
+    d = np.arange(-40, 41)
+    for alpha, beta, mu_a in ((3.0, 1.0, 0.0), (0.7, 0.45, 2.5), (12.0, 2.2, -4.25), (5.0, -0.8, 0.5)):
+        ta = -beta * math.log(alpha)
+        tm = math.asinh(-mu_a / 2.0)
+        ref = orc.prior_bias_ref(d, ta, beta, tm, eps=0.0)
+        alf = orc.prior_bias(d, alpha, beta, mu_a)
+        _close(ref, alf, 1e-12 * max(1.0, np.max(np.abs(alf))), f"reference form = alpha form ({alpha}, {beta}, {mu_a})")
+
+
+def check_ref_special_values(orc):
+    d = np.arange(-6, 7)
+    _close(orc.prior_bias_ref(d, 0.4, 0.0, 0.0), -math.exp(0.4) * np.ones(d.size), 1e-15, "theta_beta = 0: -e^theta_alpha")
+    # theta_beta = 1, eps = 0, theta_mu = 0: ALiBi with slope e^theta_alpha
+    _close(orc.prior_bias_ref(d, math.log(0.25), 1.0, 0.0, eps=0.0), -0.25 * np.abs(d), 1e-15, "ALiBi slope e^theta_alpha")
+    # at j - i = mu the bias is -e^theta_alpha eps^theta_beta (eps = 1e-5 by default)
+    tm = math.asinh(-1.5)            # mu = -3: the peak sits at i - j = 3
+    _close(orc.prior_bias_ref(np.array([3]), 0.0, 0.5, tm), [-(1e-5) ** 0.5], 1e-12, "peak value at j - i = mu")
+    _close(orc.REF_EPS, 1e-5, 0.0, "eps of the reference code")
+
+
+def check_param_derivatives_fd(orc):
+    """Central differences of the bias functions against their parameter derivatives."""
+    h = 1e-6
+    d = np.arange(-30, 31)
+    for (p1, p2, p3) in ((0.3, 0.7, 0.2), (-0.9, 1.8, -0.45), (0.1, -0.5, 0.6)):
+        for k, f in ((0, orc.prior_bias_ref_dtheta_alpha), (1, orc.prior_bias_ref_dtheta_beta),
+                     (2, orc.prior_bias_ref_dtheta_mu)):
+            pp = [p1, p2, p3]
+            pm = [p1, p2, p3]
+            pp[k] += h
+            pm[k] -= h
+            num = (orc.prior_bias_ref(d, *pp) - orc.prior_bias_ref(d, *pm)) / (2 * h)
+            _close(f(d, p1, p2, p3), num, 1e-6 * max(1.0, np.max(np.abs(num))), f"reference d/dtheta[{k}] FD")
+    dd = np.arange(-30, 31)
+    for alpha, beta, mu in ((2.0, 1.5, 0.3), (7.0, 0.6, -2.25), (4.0, -0.7, 0.5)):
+        num = (orc.prior_bias(dd, alpha, beta, mu + h) - orc.prior_bias(dd, alpha, beta, mu - h)) / (2 * h)
+        _close(orc.prior_bias_dmu(dd, alpha, beta, mu), num, 1e-6 * max(1.0, np.max(np.abs(num))), "alpha-form db/dmu FD")
+
+
 ALL_CHECKS = [
     check_worked_example, check_closed_form_offset_ssmax, check_closed_form_content,
     check_alibi_reduction, check_nope_reduction, check_gaussian_reduction, check_sqrt_reductions,
     check_brute_force, check_invariants, check_weight_ratio_law, check_decode, check_backward_fd,
     check_dalpha_alibi_closed_form, check_special_values,
+    check_ref_mu_is_two_sinh, check_ref_reduces_to_alpha_form, check_ref_special_values,
+    check_param_derivatives_fd, check_backward_fd_ref,
 ]

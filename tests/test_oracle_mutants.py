@@ -33,6 +33,17 @@ MUTANTS = {
     "bwd: dbeta sign": ("out[nz] = -np.power(u[nz], beta) * np.log(u[nz])", "out[nz] = np.power(u[nz], beta) * np.log(u[nz])"),
     "decode query position": ("np.array([n - 1]), alpha[h]", "np.array([n - 2]), alpha[h]"),
     "alpha as multiplier": ("return np.abs(x) / float(alpha)", "return np.abs(x) * float(alpha)"),
+    "ref: offset sign": ("return -np.asarray(d, np.float64) - ref_mu(theta_mu)",
+                         "return -np.asarray(d, np.float64) + ref_mu(theta_mu)"),
+    "ref: distance sign with offset": ("return -np.asarray(d, np.float64) - ref_mu(theta_mu)",
+                                       "return np.asarray(d, np.float64) - ref_mu(theta_mu)"),
+    "ref: eps dropped": ("g = np.abs(_ref_x(d, theta_mu)) + float(eps)\n    return -math.exp",
+                         "g = np.abs(_ref_x(d, theta_mu))\n    return -math.exp"),
+    "ref: mu = 2 cosh": ("return math.exp(t) - math.exp(-t)", "return math.exp(t) + math.exp(-t)"),
+    "ref: chain factor of theta_mu dropped": (" / g * (math.exp(t) + math.exp(-t))", " / g"),
+    "ref: dtheta_beta log without eps": ("return prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps) * np.log(g)",
+                                         "return prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps) * np.log(g - float(eps) + 1e-300)"),
+    "dmu sign": ("out[nz] = beta * np.power(u[nz], beta) / x[nz]", "out[nz] = -beta * np.power(u[nz], beta) / x[nz]"),
 }
 
 
