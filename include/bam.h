@@ -77,6 +77,17 @@ typedef int bam_status;
  * callers whose prior parameters do not change between calls (inference); with trained
  * parameters leave it unset.  Accepted by bam_attn_fwd and bam_attn_decode. */
 #define BAM_TABLE_READY 4u
+/* Reference parameterisation of the prior ("Bayesian Attention Mechanism" README,
+ * "Implementation Details", the formula and its AttentionPrior code): the per-head arrays
+ * alpha, beta, mu hold theta_alpha, theta_beta, theta_mu and
+ *   b_h(d) = -e^theta_alpha * ( |(j - i) - mu| + eps )^theta_beta,   d = i - j,
+ *   mu = e^theta_mu - e^-theta_mu,   eps = BAM_REF_EPS.
+ * (The page's printed formula writes (i - j) - mu; its code subtracts mu from j - i.  The
+ * two agree for theta_mu = 0, the page's default; the code's sign is used.)  mu may be
+ * NULL (theta_mu = 0).  Every value is finite for finite thetas (eps > 0), so the
+ * beta < 0 precondition does not apply.  Accepted by every entry point. */
+#define BAM_PRIOR_REF 8u
+#define BAM_REF_EPS 1e-5
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* bam_status_string(bam_status status);
@@ -100,6 +111,19 @@ int bam_version(void);
 bam_status bam_prior_table(const float* alpha, const float* beta, const float* mu, int H,
                            int d0, int n, float* tab, float* dalpha, float* dbeta,
                            void* stream);
+
+/*
+ * bam_prior_table_ex - bam_prior_table for either parameterisation, with the offset
+ * derivative.  flags: 0 (alpha-form) or BAM_PRIOR_REF.  dalpha, dbeta, dmu may each be
+ * NULL.  Alpha-form: dmu = db/dmu = beta u^beta / (d - mu) (0 where u = 0).  Reference
+ * form, with x = (j - i) - mu and g = |x| + eps:
+ *   dalpha = db/dtheta_alpha = b,   dbeta = db/dtheta_beta = b ln g,
+ *   dmu    = db/dtheta_mu    = -b theta_beta sign(x) / g * (e^theta_mu + e^-theta_mu)
+ * (sign(0) = 0).
+ */
+bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float* mu, int H,
+                              int d0, int n, unsigned flags, float* tab, float* dalpha,
+                              float* dbeta, float* dmu, void* stream);
 
 /*
  * bam_attn_fwd - prefill forward.
@@ -148,6 +172,7 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
  *   dV = P^T dout,  dQ_i = c_i sum_j dZ_ij k_j / sqrt(Dh),  dK_j = sum_i c_i dZ_ij q_i / sqrt(Dh),
  *   dalpha = sum c_i dZ_ij db/dalpha,  dbeta = sum c_i dZ_ij db/dbeta,
  *   ds = sum dZ_ij ln(n_i) (q_i.k_j / sqrt(Dh) + b_ij).
+ * With BAM_PRIOR_REF, dalpha and dbeta are the gradients in theta_alpha and theta_beta.
  * Supported: in_dtype BAM_BF16 with Dh in {32, 64}.
  */
 size_t bam_bwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
@@ -158,6 +183,21 @@ bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void*
                         unsigned flags, void* dq, void* dk, void* dv, int grad_dtype,
                         float* dalpha, float* dbeta, float* ds,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bam_attn_bwd_ex - bam_attn_bwd that also returns the gradient with respect to the
+ * offset: dmu (device float32[H]) = sum c_i dZ_ij db/dmu (alpha-form) or the gradient in
+ * theta_mu (BAM_PRIOR_REF), which the page's training code makes trainable on request.
+ * dmu may be NULL (not computed; bam_attn_bwd is this call with dmu = NULL).  Same
+ * workspace size as bam_attn_bwd.
+ */
+bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                           const float* lse, const void* dout, int in_dtype,
+                           int B, int H, int T, int Dh,
+                           const float* alpha, const float* beta, const float* mu, const float* s,
+                           unsigned flags, void* dq, void* dk, void* dv, int grad_dtype,
+                           float* dalpha, float* dbeta, float* dmu, float* ds,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,8 +13,10 @@ import ctypes
 import os
 
 __all__ = [
-    "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BamError", "lib", "lib_path",
-    "bam_prior_table", "bam_attn_fwd", "bam_attn_decode", "bam_attn_bwd",
+    "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BAM_PRIOR_REF", "BAM_REF_EPS",
+    "BamError", "lib", "lib_path",
+    "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_bwd",
+    "bam_attn_bwd_ex",
     "bam_fwd_workspace_size", "bam_decode_workspace_size", "bam_bwd_workspace_size",
     "EXPORTED_SYMBOLS",
 ]
@@ -24,15 +26,17 @@ BAM_F32 = 1
 BAM_CAUSAL = 1
 BAM_SSMAX = 2
 BAM_TABLE_READY = 4
+BAM_PRIOR_REF = 8
+BAM_REF_EPS = 1e-5
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 EXPORTED_SYMBOLS = (
-    "bam_status_string", "bam_version", "bam_prior_table",
+    "bam_status_string", "bam_version", "bam_prior_table", "bam_prior_table_ex",
     "bam_fwd_workspace_size", "bam_attn_fwd",
     "bam_decode_workspace_size", "bam_attn_decode",
-    "bam_bwd_workspace_size", "bam_attn_bwd",
+    "bam_bwd_workspace_size", "bam_attn_bwd", "bam_attn_bwd_ex",
 )
 
 
@@ -52,6 +56,8 @@ def _declare(L):
     L.bam_version.argtypes = []
     L.bam_prior_table.restype = i
     L.bam_prior_table.argtypes = [fp, fp, fp, i, i, i, fp, fp, fp, vp]
+    L.bam_prior_table_ex.restype = i
+    L.bam_prior_table_ex.argtypes = [fp, fp, fp, i, i, i, u, fp, fp, fp, fp, vp]
     L.bam_fwd_workspace_size.restype = sz
     L.bam_fwd_workspace_size.argtypes = [i, i, i, i, u]
     L.bam_attn_fwd.restype = i
@@ -65,6 +71,9 @@ def _declare(L):
     L.bam_attn_bwd.restype = i
     L.bam_attn_bwd.argtypes = [vp, vp, vp, vp, i, fp, vp, i, i, i, i, i, fp, fp, fp, fp, u,
                                vp, vp, vp, i, fp, fp, fp, vp, sz, vp]
+    L.bam_attn_bwd_ex.restype = i
+    L.bam_attn_bwd_ex.argtypes = [vp, vp, vp, vp, i, fp, vp, i, i, i, i, i, fp, fp, fp, fp, u,
+                                  vp, vp, vp, i, fp, fp, fp, fp, vp, sz, vp]
 
 
 def lib():
@@ -145,8 +154,8 @@ def _workspace(nbytes, device, workspace=None):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def _flags(causal: bool, ssmax: bool) -> int:
-    return (BAM_CAUSAL if causal else 0) | (BAM_SSMAX if ssmax else 0)
+def _flags(causal: bool, ssmax: bool, prior_ref: bool = False) -> int:
+    return (BAM_CAUSAL if causal else 0) | (BAM_SSMAX if ssmax else 0) | (BAM_PRIOR_REF if prior_ref else 0)
 
 
 # ---------------------------------------------------------------------------------------
@@ -178,14 +187,27 @@ def bam_prior_table(alpha, beta, mu, d0: int, n: int, derivatives: bool = False,
     return (tab, da, db) if derivatives else tab
 
 
+def bam_prior_table_ex(alpha, beta, mu, d0: int, n: int, prior_ref: bool = False, stream=None):
+    """(tab, dalpha, dbeta, dmu), each float32 [H, n]: the bias of distance d0 + t and its
+    derivatives in the three per-head parameters (theta's with prior_ref)."""
+    torch = _torch()
+    H = alpha.numel()
+    outs = [torch.empty((H, n), dtype=torch.float32, device=alpha.device) for _ in range(4)]
+    st = lib().bam_prior_table_ex(_dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), H, d0, n,
+                                  BAM_PRIOR_REF if prior_ref else 0, *(_ptr(t) for t in outs), _stream(stream))
+    _check(st, "bam_prior_table_ex")
+    return tuple(outs)
+
+
 def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True, o_dtype=None,
-                 o=None, lse=None, workspace=None, stream=None, table_ready=False):
+                 o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False):
     """Prefill forward; q, k, v [B, H, T, Dh].  Returns (o, lse).
 
-    table_ready: the given workspace already holds this call's distance table (BAM_TABLE_READY)."""
+    table_ready: the given workspace already holds this call's distance table (BAM_TABLE_READY).
+    prior_ref: alpha / beta / mu hold theta_alpha / theta_beta / theta_mu (BAM_PRIOR_REF)."""
     torch = _torch()
     B, H, T, Dh = q.shape
-    flags = _flags(causal, ssmax) | (BAM_TABLE_READY if table_ready else 0)
+    flags = _flags(causal, ssmax, prior_ref) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(q)
@@ -209,11 +231,11 @@ def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
 
 
 def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, ssmax=True, o_dtype=None,
-                    o=None, lse=None, workspace=None, stream=None, table_ready=False):
+                    o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False):
     """Decode; q [B, H, Dh], caches [B, H, Lmax, Dh], kv_len int32 [B].  Returns (o, lse)."""
     torch = _torch()
     B, H, Lmax, Dh = k_cache.shape
-    flags = _flags(False, ssmax) | (BAM_TABLE_READY if table_ready else 0)
+    flags = _flags(False, ssmax, prior_ref) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(k_cache)
@@ -237,11 +259,24 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
 
 
 def bam_attn_bwd(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
-                 grad_dtype=None, workspace=None, stream=None):
+                 grad_dtype=None, workspace=None, stream=None, prior_ref=False):
     """Backward.  Returns (dq, dk, dv, dalpha, dbeta, ds)."""
+    return _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream,
+                prior_ref, False)
+
+
+def bam_attn_bwd_ex(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
+                    grad_dtype=None, workspace=None, stream=None, prior_ref=False):
+    """Backward with the offset gradient.  Returns (dq, dk, dv, dalpha, dbeta, dmu, ds)."""
+    return _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream,
+                prior_ref, True)
+
+
+def _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream, prior_ref,
+         want_mu):
     torch = _torch()
     B, H, T, Dh = q.shape
-    flags = _flags(causal, ssmax)
+    flags = _flags(causal, ssmax, prior_ref)
     in_code = _dtype_code(q)
     gc = in_code if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
     gdt = _torch_dtype(gc)
@@ -250,14 +285,19 @@ def bam_attn_bwd(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=Tru
     dv = torch.empty_like(q, dtype=gdt)
     dalpha = torch.empty(H, dtype=torch.float32, device=q.device)
     dbeta = torch.empty_like(dalpha)
+    dmu = torch.empty_like(dalpha) if want_mu else None
     ds = torch.empty_like(dalpha)
     nb = bam_bwd_workspace_size(B, H, T, Dh, flags)
     ws = _workspace(nb, q.device, workspace)
     a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
-    st = lib().bam_attn_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dtype_code(o),
-                            _dev(lse, "lse"), _dev(dout, "dout"), in_code, B, H, T, Dh, a, b_, m_, s_, flags,
-                            _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), gc, _dev(dalpha, "dalpha"),
-                            _dev(dbeta, "dbeta"), _dev(ds, "ds"), _ptr(ws), ws.numel() * ws.element_size(),
-                            _stream(stream))
+    head = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dtype_code(o), _dev(lse, "lse"),
+            _dev(dout, "dout"), in_code, B, H, T, Dh, a, b_, m_, s_, flags, _dev(dq, "dq"), _dev(dk, "dk"),
+            _dev(dv, "dv"), gc, _dev(dalpha, "dalpha"), _dev(dbeta, "dbeta"))
+    tail = (_dev(ds, "ds"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if want_mu:
+        st = lib().bam_attn_bwd_ex(*head, _dev(dmu, "dmu"), *tail)
+        _check(st, "bam_attn_bwd_ex")
+        return dq, dk, dv, dalpha, dbeta, dmu, ds
+    st = lib().bam_attn_bwd(*head, *tail)
     _check(st, "bam_attn_bwd")
     return dq, dk, dv, dalpha, dbeta, ds

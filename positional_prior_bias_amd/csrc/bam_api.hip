@@ -73,8 +73,17 @@ int bam_version(void) { return 100; }
 bam_status bam_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
                            int n, float* tab, float* dalpha, float* dbeta, void* stream) {
   if (alpha == nullptr || beta == nullptr || tab == nullptr || H <= 0 || n <= 0) return BAM_EINVAL;
-  return hip_status(bam::launch_prior_table(alpha, beta, mu, H, d0, n, n, 1.0f, tab, dalpha, dbeta,
-                                            (hipStream_t)stream));
+  return hip_status(bam::launch_prior_table(alpha, beta, mu, false, H, d0, n, n, 1.0f, tab, dalpha, dbeta,
+                                            nullptr, (hipStream_t)stream));
+}
+
+bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float* mu, int H, int d0,
+                              int n, unsigned flags, float* tab, float* dalpha, float* dbeta, float* dmu,
+                              void* stream) {
+  if (alpha == nullptr || beta == nullptr || tab == nullptr || H <= 0 || n <= 0) return BAM_EINVAL;
+  if ((flags & ~BAM_PRIOR_REF) != 0) return BAM_EINVAL;
+  return hip_status(bam::launch_prior_table(alpha, beta, mu, (flags & BAM_PRIOR_REF) != 0, H, d0, n, n, 1.0f,
+                                            tab, dalpha, dbeta, dmu, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -94,7 +103,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       lse == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   if (in_dtype == BAM_BF16) {
     if (Dh != 32 && Dh != 64 && Dh != 128) return BAM_EUNSUPPORTED;
@@ -107,6 +116,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (workspace_bytes < bam_fwd_workspace_size(B, H, T, Dh, flags)) return BAM_EWORKSPACE;
 
   const bool causal = (flags & BAM_CAUSAL) != 0;
+  const bool ref = (flags & BAM_PRIOR_REF) != 0;
   const bool bf16 = in_dtype == BAM_BF16;
   const TableGeom g = bf16 ? fwd_table_geom(T, causal) : table_geom(T, causal);
   hipStream_t st = (hipStream_t)stream;
@@ -114,10 +124,11 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   hipError_t e = hipSuccess;
   if (!(flags & BAM_TABLE_READY)) {
     if (bf16)
-      e = bam::launch_prior_table_ex(alpha, beta, mu, H, g.d0, -1, g.n, g.stride, causal ? 0 : -(T - 1), T - 1,
-                                     std::sqrt((float)Dh), tab, nullptr, nullptr, st);
+      e = bam::launch_prior_table_ex(alpha, beta, mu, ref, H, g.d0, -1, g.n, g.stride, causal ? 0 : -(T - 1), T - 1,
+                                     std::sqrt((float)Dh), tab, nullptr, nullptr, nullptr, st);
     else
-      e = bam::launch_prior_table(alpha, beta, mu, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr, st);
+      e = bam::launch_prior_table(alpha, beta, mu, ref, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr,
+                                  nullptr, st);
     if (e != hipSuccess) return BAM_EHIP;
   }
   bam::FwdArgs a;
@@ -173,7 +184,7 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
       !aligned16(o) || lse == nullptr || kv_len == nullptr || workspace == nullptr ||
       !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   const DecodeLayout L = decode_layout(B, H, Lmax, Dh);
@@ -181,7 +192,8 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
   hipStream_t st = (hipStream_t)stream;
   float* tab = (float*)((char*)workspace + L.tab_off);
   if (!(flags & BAM_TABLE_READY)) {
-    hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, 0, Lmax, L.tab_stride, 1.0f, tab, nullptr, nullptr, st);
+    hipError_t e = bam::launch_prior_table(alpha, beta, mu, (flags & BAM_PRIOR_REF) != 0, H, 0, Lmax, L.tab_stride,
+                                           1.0f, tab, nullptr, nullptr, nullptr, st);
     if (e != hipSuccess) return BAM_EHIP;
   }
   bam::DecodeArgs a;
@@ -208,7 +220,7 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
 // ---------------------------------------------------------------------------------------
 namespace {
 struct BwdLayout {
-  size_t tab_off, ta_off, tb_off, D_off, part_off, total;
+  size_t tab_off, ta_off, tb_off, tm_off, D_off, part_off, total;
   TableGeom g;
 };
 
@@ -219,7 +231,8 @@ BwdLayout bwd_layout(int B, int H, int T, bool causal) {
   L.tab_off = 0;
   L.ta_off = tabsz;
   L.tb_off = 2 * tabsz;
-  L.D_off = 3 * tabsz;
+  L.tm_off = 3 * tabsz;
+  L.D_off = 4 * tabsz;
   L.part_off = L.D_off + align_up((size_t)B * H * T * sizeof(float));
   L.total = L.part_off + align_up(bam::bwd_param_partials(B, H, T) * sizeof(float));
   return L;
@@ -238,12 +251,22 @@ bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void*
                         unsigned flags, void* dq, void* dk, void* dv, int grad_dtype, float* dalpha,
                         float* dbeta, float* ds, void* workspace, size_t workspace_bytes,
                         void* stream) {
+  return bam_attn_bwd_ex(q, k, v, o, o_dtype, lse, dout, in_dtype, B, H, T, Dh, alpha, beta, mu, s, flags, dq,
+                         dk, dv, grad_dtype, dalpha, dbeta, nullptr, ds, workspace, workspace_bytes, stream);
+}
+
+bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, int o_dtype,
+                           const float* lse, const void* dout, int in_dtype, int B, int H, int T, int Dh,
+                           const float* alpha, const float* beta, const float* mu, const float* s,
+                           unsigned flags, void* dq, void* dk, void* dv, int grad_dtype, float* dalpha,
+                           float* dbeta, float* dmu, float* ds, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || lse == nullptr ||
       dalpha == nullptr || dbeta == nullptr || ds == nullptr || workspace == nullptr ||
       !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64)) return BAM_EUNSUPPORTED;
   if ((o_dtype != BAM_BF16 && o_dtype != BAM_F32) || (grad_dtype != BAM_BF16 && grad_dtype != BAM_F32))
     return BAM_EUNSUPPORTED;
@@ -255,7 +278,9 @@ bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void*
   float* tab = (float*)(ws + L.tab_off);
   float* ta = (float*)(ws + L.ta_off);
   float* tb = (float*)(ws + L.tb_off);
-  hipError_t e = bam::launch_prior_table(alpha, beta, mu, H, L.g.d0, L.g.n, L.g.stride, 1.0f, tab, ta, tb, st);
+  float* tm = dmu ? (float*)(ws + L.tm_off) : nullptr;
+  hipError_t e = bam::launch_prior_table(alpha, beta, mu, (flags & BAM_PRIOR_REF) != 0, H, L.g.d0, L.g.n,
+                                         L.g.stride, 1.0f, tab, ta, tb, tm, st);
   if (e != hipSuccess) return BAM_EHIP;
   bam::BwdArgs a;
   a.q = q;
@@ -268,6 +293,7 @@ bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void*
   a.tab = tab;
   a.tab_da = ta;
   a.tab_db = tb;
+  a.tab_dm = tm;
   a.s = s;
   a.tab_d0 = L.g.d0;
   a.tab_stride = L.g.stride;
@@ -285,6 +311,7 @@ bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void*
   a.grad_f32 = grad_dtype == BAM_F32;
   a.dalpha = dalpha;
   a.dbeta = dbeta;
+  a.dmu = dmu;
   a.ds = ds;
   return hip_status(bam::launch_bwd(a, Dh, st));
 }

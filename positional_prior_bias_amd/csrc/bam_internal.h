@@ -7,15 +7,16 @@
 
 namespace bam {
 
-// Launch the distance-table kernel: tab[h*stride + t] = b_h(d0 + t) (and derivatives).
-hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
-                              int n, int stride, float scale, float* tab, float* dalpha, float* dbeta,
-                              hipStream_t stream);
+// Launch the distance-table kernel: tab[h*stride + t] = b_h(d0 + t) (and derivatives;
+// any derivative pointer may be null).  ref: reference parameterisation (theta's).
+hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, bool ref, int H,
+                              int d0, int n, int stride, float scale, float* tab, float* dalpha,
+                              float* dbeta, float* dmu, hipStream_t stream);
 // General form: entry t holds d = d_first + step * t; entries with d outside [dlo, dhi]
 // are padding (-inf bias, zero derivatives).  The bias is multiplied by `scale`.
-hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, int H, int d_first,
-                                 int step, int n, int stride, int dlo, int dhi, float scale, float* tab,
-                                 float* dalpha, float* dbeta, hipStream_t stream);
+hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, bool ref, int H,
+                                 int d_first, int step, int n, int stride, int dlo, int dhi, float scale,
+                                 float* tab, float* dalpha, float* dbeta, float* dmu, hipStream_t stream);
 
 // Forward distance table: reversed (entry u holds d = dhi + kFwdTabPad - u), padded by
 // kFwdTabPad entries of -inf on both sides and scaled by sqrt(Dh), so every per-tile
@@ -72,6 +73,7 @@ struct BwdArgs {
   const float* tab;      // bias b(d), index d (causal: 0..T-1; else d + T - 1)
   const float* tab_da;   // db/dalpha
   const float* tab_db;   // db/dbeta
+  const float* tab_dm;   // db/dmu (null: dmu not wanted)
   const float* s;
   int tab_d0;
   int tab_stride;
@@ -86,6 +88,7 @@ struct BwdArgs {
   bool grad_f32;
   float* dalpha;
   float* dbeta;
+  float* dmu;            // null: not computed
   float* ds;
 };
 

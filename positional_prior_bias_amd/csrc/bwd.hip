@@ -18,7 +18,7 @@
 //              (one query per lane), walks the key tiles: dQ^T += K^T dZ^T, and the
 //              per-element parameter terms are accumulated here, one partial per
 //              work-group (no atomics: the reduction order is fixed).
-//   bwd_params sums the partials of each head.
+//   bwd_params sums the partials of each head (alpha, beta, s and, when wanted, mu).
 // The bias is again the accumulator's initial value (sqrt(Dh) b from the distance
 // window in LDS, -inf where the causal mask forbids the pair).
 #include <float.h>
@@ -239,7 +239,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
 }
 
 // ------------------------------------------------------------------------------------
-template <int DH, bool CAUSAL>
+// MU: also accumulate the offset term c dZ db/dmu (db/dmu table tab_dm).
+template <int DH, bool CAUSAL, bool MU>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
@@ -250,7 +251,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   __shared__ float tw[TW];
   __shared__ float twa[TW];
   __shared__ float twb[TW];
-  __shared__ float red[3][4];
+  __shared__ float twm[MU ? TW : 1];
+  __shared__ float red[4][4];
 
   const int BH = a.B * a.H;
   const int qb = blockIdx.x / BH;
@@ -298,13 +300,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) dq[db][x] = 0.f;
-  float ga = 0.f, gb = 0.f, gs = 0.f;
+  float ga = 0.f, gb = 0.f, gs = 0.f, gm = 0.f;
 
   const int kend = CAUSAL ? min(T, i0 + kMQ) : T;
   const int ntiles = (kend + kNK - 1) / kNK;
   const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
   const float* __restrict__ tabah = a.tab_da + (size_t)h * a.tab_stride;
   const float* __restrict__ tabbh = a.tab_db + (size_t)h * a.tab_stride;
+  const float* __restrict__ tabmh = MU ? a.tab_dm + (size_t)h * a.tab_stride : nullptr;
   const int dlo = CAUSAL ? 0 : -(T - 1);
   const int dhi = T - 1;
 
@@ -321,6 +324,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
       tw[x] = ok ? sqrtD * tabh[d - a.tab_d0] : kNegInf;
       twa[x] = ok ? tabah[d - a.tab_d0] : 0.f;
       twb[x] = ok ? tabbh[d - a.tab_d0] : 0.f;
+      if (MU) twm[x] = ok ? tabmh[d - a.tab_d0] : 0.f;
     }
     __syncthreads();
 
@@ -353,6 +357,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
         const float cz = c * z;
         ga = fmaf(cz, twa[widx], ga);
         gb = fmaf(cz, twb[widx], gb);
+        if (MU) gm = fmaf(cz, twm[widx], gm);
         gs = fmaf(z * lnn_sd, fmaxf(sx, -FLT_MAX), gs);
       }
 #pragma unroll
@@ -393,29 +398,32 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     ga += __shfl_xor(ga, off, 64);
     gb += __shfl_xor(gb, off, 64);
     gs += __shfl_xor(gs, off, 64);
+    if (MU) gm += __shfl_xor(gm, off, 64);
   }
   if (lane == 0) {
     red[0][wave] = ga;
     red[1][wave] = gb;
     red[2][wave] = gs;
+    red[3][wave] = gm;
   }
   __syncthreads();
-  if (tid < 3) {
+  if (tid < 4) {
     const float v = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
-    a.param_part[(((size_t)h * a.B + b) * nqb + qb) * 3 + tid] = v;
+    a.param_part[(((size_t)h * a.B + b) * nqb + qb) * 4 + tid] = v;
   }
 }
 
 // ------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) bwd_params_kernel(BwdArgs a, int nper) {
-  const int k = blockIdx.x;   // 0: alpha, 1: beta, 2: s
+  const int k = blockIdx.x;   // 0: alpha, 1: beta, 2: s, 3: mu
   const int h = blockIdx.y;
   double acc = 0.0;
-  for (int x = threadIdx.x; x < nper; x += 64) acc += (double)a.param_part[((size_t)h * nper + x) * 3 + k];
+  if (k == 3 && a.dmu == nullptr) return;
+  for (int x = threadIdx.x; x < nper; x += 64) acc += (double)a.param_part[((size_t)h * nper + x) * 4 + k];
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
   if (threadIdx.x == 0) {
-    float* out = k == 0 ? a.dalpha : (k == 1 ? a.dbeta : a.ds);
+    float* out = k == 0 ? a.dalpha : (k == 1 ? a.dbeta : (k == 2 ? a.ds : a.dmu));
     out[h] = (k == 2 && !a.ssmax) ? 0.f : (float)acc;
   }
 }
@@ -434,17 +442,21 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (a.T + kMQ - 1) / kMQ;
-  hipLaunchKernelGGL((bwd_dq_kernel<DH, CAUSAL>), dim3((unsigned)(nqb * a.B * a.H)), dim3(256), 0, stream,
-                     a, nqb);
+  if (a.tab_dm)
+    hipLaunchKernelGGL((bwd_dq_kernel<DH, CAUSAL, true>), dim3((unsigned)(nqb * a.B * a.H)), dim3(256), 0,
+                       stream, a, nqb);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<DH, CAUSAL, false>), dim3((unsigned)(nqb * a.B * a.H)), dim3(256), 0,
+                       stream, a, nqb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_params_kernel, dim3(3, a.H), dim3(64), 0, stream, a, a.B * nqb);
+  hipLaunchKernelGGL(bwd_params_kernel, dim3(4, a.H), dim3(64), 0, stream, a, a.B * nqb);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_param_partials(int B, int H, int T) { return (size_t)H * B * ((T + kMQ - 1) / kMQ) * 3; }
+size_t bwd_param_partials(int B, int H, int T) { return (size_t)H * B * ((T + kMQ - 1) / kMQ) * 4; }
 
 hipError_t launch_bwd(const BwdArgs& a, int Dh, hipStream_t stream) {
   switch (Dh) {

@@ -218,6 +218,31 @@ def random_case(seed: int, B: int, H: int, T: int, Dh: int, dtype: str = "bf16",
     return w
 
 
+def ref_case(seed: int, B: int, H: int, T: int, Dh: int, dtype: str = "bf16", flags: int = CAUSAL | SSMAX,
+             theta_alpha_range=(-3.0, 0.5), theta_beta_range=(0.0, 1.0), theta_mu_range=(-0.5, 0.5),
+             s_range=(0.3, 0.6), with_grad: bool = False) -> Workload:
+    """Small case in the reference parameterisation: the workload's alpha / beta / mu
+    arrays hold theta_alpha / theta_beta / theta_mu.
+
+    The default theta_beta range is the page's linspace(0, 1) head initialisation
+    ("Bayesian Attention Mechanism" README, "Implementation Details").  Draw order: Q, K,
+    V, theta_alpha ~ U, theta_beta ~ U, theta_mu ~ U, s ~ U, then dO if requested.
+    """
+    rng = np.random.default_rng(seed)
+    bf = dtype == "bf16"
+    q = _normal(rng, (B, H, T, Dh), bf)
+    k = _normal(rng, (B, H, T, Dh), bf)
+    v = _normal(rng, (B, H, T, Dh), bf)
+    ta = rng.uniform(*theta_alpha_range, H).astype(np.float32)
+    tb = rng.uniform(*theta_beta_range, H).astype(np.float32)
+    tm = rng.uniform(*theta_mu_range, H).astype(np.float32)
+    s = rng.uniform(s_range[0], s_range[1], H).astype(np.float32)
+    w = Workload("ref_T%d" % T, B, H, T, Dh, dtype, flags, ta, tb, tm, s, q, k, v)
+    if with_grad:
+        w.do = _normal(rng, (B, H, T, Dh), bf)
+    return w
+
+
 def alibi_slopes(H: int) -> np.ndarray:
     """Per-head ALiBi slopes m_h = 2^(-8(h+1)/H) for every H.
 
