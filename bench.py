@@ -172,6 +172,25 @@ def bench_decode(torch, bam, w, steps, warmup, timer):
                 kernels_gbs=nbytes / kern_ms / 1e6)
 
 
+def bench_train_step(torch, w, steps, warmup, timer):
+    """Forward + backward through the autograd module (reference parameterisation, every
+    prior parameter trained, SSMax on), gradients for q, k, v and the prior."""
+    from positional_prior_bias_amd.autograd import BamAttention
+    m = BamAttention(w.q.shape[1], max_seq_len=w.q.shape[2], train_theta_mu=True, device="cuda")
+    x = device_inputs(torch, w, with_grad=True)
+    q, k, v = (x[n].requires_grad_(True) for n in ("q", "k", "v"))
+    do = x["do"]
+
+    def step():
+        for t in [q, k, v] + list(m.parameters()):
+            t.grad = None
+        o = m(q, k, v)
+        o.backward(do)
+    ms, wall = timer.steps(step, steps, warmup)
+    log(f"[train512] step {ms:.4f} ms (wall {wall:.4f})")
+    return dict(ms=ms, wall_ms=wall)
+
+
 def cpu_baseline(w, seconds):
     """fp64 oracle on whole (b, h) heads of the same batch until `seconds` have elapsed."""
     import oracle
@@ -215,8 +234,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--parts", default="fwd512,fwd32k,decode,fwdbwd512",
-                    help="comma list of fwd512,fwd32k,decode,fwdbwd512 (fwd512 is always run)")
+    ap.add_argument("--parts", default="fwd512,fwd32k,decode,fwdbwd512,train512",
+                    help="comma list of fwd512,fwd32k,decode,fwdbwd512,train512 (fwd512 is always run)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -287,6 +306,13 @@ def main():
             "ms": round(r["ms"], 4), "TFLOP/s": round(r["tflops"], 1),
             "pct_mfma_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
             "bwd_call_ms": round(r["bwd_call_ms"], 4), "bwd_TFLOP/s": round(r["bwd_tflops"], 1)}
+        if "train512" in parts:
+            r = bench_train_step(torch, w3, args.steps, args.warmup, timer)
+            out_parts["train_step_T512"] = {
+                "workload": "autograd step through BamAttention at B=32 H=12 T=512 Dh=64: forward + backward, "
+                            "grads for q, k, v, theta_alpha, theta_beta, theta_mu, s",
+                "ms": round(r["ms"], 4), "wall_ms": round(r["wall_ms"], 4),
+                "TFLOP/s": round(14.0 * 64 * 32 * 12 * 512 * 513 / 2 / r["ms"] / 1e9, 1)}
         del w3
 
     if args.copy_calibration:
