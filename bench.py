@@ -191,6 +191,27 @@ def bench_train_step(torch, w, steps, warmup, timer):
     return dict(ms=ms, wall_ms=wall)
 
 
+def bench_sweep(torch, bam, wl, timer):
+    """Passkey-style length sweep: causal prefill at T = 1k .. 32k (32,768 tokens per batch)
+    and decode against caches of 4k .. 512k tokens (B = 8, one planted key per sequence)."""
+    out = {"prefill": [], "decode": []}
+    for T in (1024, 4096, 16384, 32768):
+        w = wl.long_prefill(T=T, B=max(1, 32768 // T))
+        r = bench_fwd(torch, bam, w, 5, 2, timer, f"sweep fwd T={T}")
+        out["prefill"].append({"T": T, "B": w.q.shape[0], "kernel_ms": round(r["kernel_ms"], 4),
+                               "kernel_TFLOP/s": round(r["kernel_tflops"], 1),
+                               "step_TFLOP/s": round(r["tflops"], 1)})
+        del w
+    for L in (4096, 32768, 131072, 262144, 524288):
+        w = wl.long_decode_device(L=L)
+        r = bench_decode(torch, bam, w, 5, 2, timer)
+        out["decode"].append({"L": L, "step_ms": round(r["ms"], 4), "step_GB/s": round(r["gbs"], 1),
+                              "kernels_GB/s": round(r["kernels_gbs"], 1)})
+        del w
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, seconds):
     """fp64 oracle on whole (b, h) heads of the same batch until `seconds` have elapsed."""
     import oracle
@@ -235,7 +256,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--parts", default="fwd512,fwd32k,decode,fwdbwd512,train512",
-                    help="comma list of fwd512,fwd32k,decode,fwdbwd512,train512 (fwd512 is always run)")
+                    help="comma list of fwd512,fwd32k,decode,fwdbwd512,train512,sweep (fwd512 is always "
+                         "run; sweep, the length sweep, is not run by default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -314,6 +336,9 @@ def main():
                 "ms": round(r["ms"], 4), "wall_ms": round(r["wall_ms"], 4),
                 "TFLOP/s": round(14.0 * 64 * 32 * 12 * 512 * 513 / 2 / r["ms"] / 1e9, 1)}
         del w3
+
+    if "sweep" in parts:
+        out_parts["length_sweep"] = bench_sweep(torch, bam, wl, timer)
 
     if args.copy_calibration:
         n = 512 << 20

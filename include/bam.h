@@ -161,6 +161,28 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bam_attn_decode_paged - bam_attn_decode on a paged KV cache.
+ *
+ * k_pages, v_pages: [num_pages, H, page_size, Dh] of in_dtype; block_table: device
+ * int32[B, max_blocks], entry p of sequence b = the page holding its keys
+ * p * page_size .. (p + 1) * page_size - 1.  kv_len as for bam_attn_decode, with
+ * Lmax = max_blocks * page_size.  page_size must be a multiple of 64 (BAM_EUNSUPPORTED
+ * otherwise).  Preconditions: 0 <= block_table entries < num_pages for the pages a
+ * sequence uses (out-of-range ids are clamped, so a bad table gives wrong values but
+ * never reads outside the pages).  Workspace: bam_decode_workspace_size(B, H,
+ * max_blocks * page_size, Dh).  Same result as bam_attn_decode on the gathered cache.
+ * Serving systems keep caches in pages so sequences of different lengths share one pool
+ * ("Bayesian Attention Mechanism" README, "Highlights": decoding far beyond the
+ * training context).
+ */
+bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int in_dtype,
+                                 const int32_t* block_table, int max_blocks, int num_pages, int page_size,
+                                 const int32_t* kv_len, int B, int H, int Dh,
+                                 const float* alpha, const float* beta, const float* mu, const float* s,
+                                 unsigned flags, void* o, int o_dtype, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bam_attn_bwd - backward of bam_attn_fwd for L = sum(O * dout).
  *
  * q, k, v, dout: [B, H, T, Dh] of in_dtype; o: the forward output, [B, H, T, Dh] of

@@ -15,7 +15,8 @@ import os
 __all__ = [
     "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BAM_PRIOR_REF", "BAM_REF_EPS",
     "BamError", "lib", "lib_path",
-    "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_bwd",
+    "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_decode_paged",
+    "bam_attn_bwd",
     "bam_attn_bwd_ex",
     "bam_fwd_workspace_size", "bam_decode_workspace_size", "bam_bwd_workspace_size",
     "EXPORTED_SYMBOLS",
@@ -35,7 +36,7 @@ _LIB = None
 EXPORTED_SYMBOLS = (
     "bam_status_string", "bam_version", "bam_prior_table", "bam_prior_table_ex",
     "bam_fwd_workspace_size", "bam_attn_fwd",
-    "bam_decode_workspace_size", "bam_attn_decode",
+    "bam_decode_workspace_size", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_bwd_workspace_size", "bam_attn_bwd", "bam_attn_bwd_ex",
 )
 
@@ -66,6 +67,9 @@ def _declare(L):
     L.bam_decode_workspace_size.argtypes = [i, i, i, i]
     L.bam_attn_decode.restype = i
     L.bam_attn_decode.argtypes = [vp, vp, vp, i, vp, i, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp, sz, vp]
+    L.bam_attn_decode_paged.restype = i
+    L.bam_attn_decode_paged.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp,
+                                        sz, vp]
     L.bam_bwd_workspace_size.restype = sz
     L.bam_bwd_workspace_size.argtypes = [i, i, i, i, u]
     L.bam_attn_bwd.restype = i
@@ -255,6 +259,38 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
                                _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
                                _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "bam_attn_decode")
+    return o, lse
+
+
+def bam_attn_decode_paged(q, k_pages, v_pages, block_table, kv_len, alpha, beta, mu=None, s=None, ssmax=True,
+                          o_dtype=None, o=None, lse=None, workspace=None, stream=None, table_ready=False,
+                          prior_ref=False):
+    """Decode on a paged cache: q [B, H, Dh]; k_pages, v_pages [num_pages, H, page_size, Dh];
+    block_table int32 [B, max_blocks]; kv_len int32 [B].  Returns (o, lse)."""
+    torch = _torch()
+    num_pages, H, page_size, Dh = k_pages.shape
+    B, max_blocks = block_table.shape
+    flags = _flags(False, ssmax, prior_ref) | (BAM_TABLE_READY if table_ready else 0)
+    if table_ready and workspace is None:
+        raise BamError("table_ready needs the workspace of an earlier call")
+    in_code = _dtype_code(k_pages)
+    if kv_len.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise BamError("kv_len and block_table must be int32")
+    oc = in_code if o_dtype is None else _dtype_code(torch.empty(0, dtype=o_dtype))
+    if o is None:
+        o = torch.empty((B, H, Dh), dtype=_torch_dtype(oc), device=q.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nb = bam_decode_workspace_size(B, H, max_blocks * page_size, Dh)
+    ws = _workspace(nb, q.device, workspace)
+    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    st = lib().bam_attn_decode_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"), in_code,
+                                     _dev(block_table, "block_table"), max_blocks, num_pages, page_size,
+                                     _dev(kv_len, "kv_len"), B, H, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
+                                     _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "bam_attn_decode_paged")
     return o, lse
 
 

@@ -175,14 +175,14 @@ size_t bam_decode_workspace_size(int B, int H, int Lmax, int Dh) {
   return decode_layout(B, H, Lmax, Dh).total;
 }
 
-bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
-                           const int32_t* kv_len, int B, int H, int Lmax, int Dh, const float* alpha,
-                           const float* beta, const float* mu, const float* s, unsigned flags, void* o,
-                           int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  if (!dims_ok(B, H, Lmax) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(o) || lse == nullptr || kv_len == nullptr || workspace == nullptr ||
-      !prior_ok(alpha, beta, s, flags))
+namespace {
+bam_status decode_common(const void* q, const void* k, const void* v, int in_dtype, const int32_t* block_table,
+                         int max_blocks, int num_pages, int page_size, const int32_t* kv_len, int B, int H,
+                         int Lmax, int Dh, const float* alpha, const float* beta, const float* mu,
+                         const float* s, unsigned flags, void* o, int o_dtype, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!dims_ok(B, H, Lmax) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      lse == nullptr || kv_len == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
   if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
@@ -198,8 +198,12 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
   }
   bam::DecodeArgs a;
   a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
+  a.k = k;
+  a.v = v;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
   a.kv_len = kv_len;
   a.tab = tab;
   a.s = s;
@@ -215,6 +219,30 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
   a.o_f32 = o_dtype == BAM_F32;
   a.lse = lse;
   return hip_status(bam::launch_decode(a, Dh, st));
+}
+}  // namespace
+
+bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                           const int32_t* kv_len, int B, int H, int Lmax, int Dh, const float* alpha,
+                           const float* beta, const float* mu, const float* s, unsigned flags, void* o,
+                           int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode_common(q, k_cache, v_cache, in_dtype, nullptr, 0, 0, 0, kv_len, B, H, Lmax, Dh, alpha, beta, mu, s,
+                       flags, o, o_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int in_dtype,
+                                 const int32_t* block_table, int max_blocks, int num_pages, int page_size,
+                                 const int32_t* kv_len, int B, int H, int Dh, const float* alpha,
+                                 const float* beta, const float* mu, const float* s, unsigned flags, void* o,
+                                 int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (block_table == nullptr || max_blocks <= 0 || num_pages <= 0 || page_size <= 0) return BAM_EINVAL;
+  if (page_size % 64 != 0) return BAM_EUNSUPPORTED;
+  if ((long)max_blocks * page_size > (long)INT32_MAX / 2) return BAM_EUNSUPPORTED;
+  return decode_common(q, k_pages, v_pages, in_dtype, block_table, max_blocks, num_pages, page_size, kv_len, B, H,
+                       max_blocks * page_size, Dh, alpha, beta, mu, s, flags, o, o_dtype, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -43,8 +43,10 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int Dh, hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;        // [B,H,Dh]
-  const void* k;        // [B,H,Lmax,Dh]
+  const void* k;        // [B,H,Lmax,Dh], or pages [num_pages,H,page_size,Dh] with a block table
   const void* v;
+  const int32_t* block_table;   // [B, max_blocks] page ids, or null (contiguous caches)
+  int max_blocks, num_pages, page_size;
   const int32_t* kv_len;
   const float* tab;     // [H][tab_stride], index = d (0 .. Lmax-1)
   const float* s;

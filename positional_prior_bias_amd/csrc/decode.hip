@@ -18,6 +18,11 @@
 //     merges the ranges exactly by their log-sum-exp.
 // The bias of distance d comes from the per-head table (one float per key, read
 // through L2, shared by every sequence of the batch).
+// Paged caches (PAGED): K and V live in pages [num_pages, H, page_size, Dh] and
+// block_table[b][p] names the page that holds keys p * page_size .. of sequence b.
+// page_size is a multiple of 64, so a wave tile never straddles two pages and costs one
+// scalar table read; page ids are clamped to [0, num_pages) so a bad table cannot read
+// outside the pages.
 #include <float.h>
 
 #include "bam_device.h"
@@ -49,7 +54,7 @@ __device__ __forceinline__ float dot8(const float* q, const u32x4& w) {
   return acc;
 }
 
-template <int DH>
+template <int DH, bool PAGED>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   using S = DecodeShape<DH>;
   constexpr int LPK = S::LPK, KPI = S::KPI, KT = S::KT;
@@ -84,7 +89,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const float c = ssmax_c(a.ssmax, a.ssmax ? a.s[h] : 1.0f, L);
   const float C = fmaxf(c, FLT_MIN);
   const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
-  const size_t kvbase = (size_t)bh * a.Lmax * DH;
+  const size_t kvbase = PAGED ? 0 : (size_t)bh * a.Lmax * DH;
   const uint16_t* __restrict__ Kc = (const uint16_t*)a.k + kvbase;
   const uint16_t* __restrict__ Vc = (const uint16_t*)a.v + kvbase;
 
@@ -94,16 +99,27 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int tb = kbeg + wave * KT; tb < kend; tb += kWaves * KT) {
+    // rows of this tile: Kt / Vt + (tile-relative key) * DH
+    const uint16_t* __restrict__ Kt = Kc + (size_t)tb * DH;
+    const uint16_t* __restrict__ Vt = Vc + (size_t)tb * DH;
+    if (PAGED) {
+      const int lp = tb / a.page_size;
+      int pg = a.block_table[(size_t)b * a.max_blocks + lp];
+      pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+      const size_t pbase = (((size_t)pg * a.H + h) * a.page_size + (tb - lp * a.page_size)) * DH;
+      Kt = (const uint16_t*)a.k + pbase;
+      Vt = (const uint16_t*)a.v + pbase;
+    }
     u32x4 kw[kRows], vw[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      const int key = tb + r * KPI + slot;
+      const int kr = r * KPI + slot;
       const u32x4 z = {0u, 0u, 0u, 0u};
       kw[r] = z;
       vw[r] = z;
-      if (key < kend) {
-        kw[r] = __builtin_nontemporal_load((const u32x4*)(Kc + (size_t)key * DH + cl * 8));
-        vw[r] = __builtin_nontemporal_load((const u32x4*)(Vc + (size_t)key * DH + cl * 8));
+      if (tb + kr < kend) {
+        kw[r] = __builtin_nontemporal_load((const u32x4*)(Kt + (size_t)kr * DH + cl * 8));
+        vw[r] = __builtin_nontemporal_load((const u32x4*)(Vt + (size_t)kr * DH + cl * 8));
       }
     }
     float lg[kRows];
@@ -227,7 +243,10 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
 
 template <int DH>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel<DH>, dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  if (a.block_table)
+    hipLaunchKernelGGL((decode_split_kernel<DH, true>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<DH, false>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3(a.B * a.H), dim3(256), 0, stream, a);

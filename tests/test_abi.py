@@ -115,3 +115,7 @@ def test_decode_and_bwd_reject_bad_arguments(L):
                            16, 16, 16, 16, 256, 1 << 20, None)
     assert st == 1                                 # unknown flag bit
     assert L.bam_prior_table_ex(16, 16, None, 1, 0, 8, 1, 16, None, None, None, None) == 1   # only PRIOR_REF
+    pg = L.bam_attn_decode_paged
+    assert pg(16, 16, 16, 0, 16, 4, 8, 96, 16, 1, 1, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None) == 2
+    assert pg(16, 16, 16, 0, None, 4, 8, 64, 16, 1, 1, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None) == 1
+    assert pg(16, 16, 16, 0, 16, 0, 8, 64, 16, 1, 1, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None) == 1
