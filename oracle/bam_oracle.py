@@ -30,6 +30,8 @@ softmax, no split-KV, no distance table):
   positions[j] - positions[i]; the two agree for mu = 0 (the default, theta_mu = 0)
   and the code's sign is adopted here.  param="ref" selects it; the alpha / beta / mu
   arrays then hold theta_alpha / theta_beta / theta_mu.
+* Sandwich (attention-gym "Score Mods", "Sandwich"), param="sandwich": alpha holds the
+  per-head compression ratio and beta d_bar; see prior_bias_sandwich.
 
 Pins (tests/test_oracle_pins.py) tie this module to things other than itself:
 the printed ALiBi worked example, torch's scaled_dot_product_attention on the
@@ -47,7 +49,7 @@ import numpy as np
 __all__ = [
     "prior_bias", "prior_bias_dalpha", "prior_bias_dbeta", "prior_bias_dmu", "ssmax_factor",
     "REF_EPS", "ref_mu", "prior_bias_ref", "prior_bias_ref_dtheta_alpha", "prior_bias_ref_dtheta_beta",
-    "prior_bias_ref_dtheta_mu",
+    "prior_bias_ref_dtheta_mu", "prior_bias_sandwich", "sandwich_ratios",
     "attn_fwd", "attn_fwd_rows", "attn_decode", "attn_bwd", "attention_probs",
 ]
 
@@ -181,6 +183,33 @@ def prior_bias_ref_dtheta_mu(d, theta_alpha, theta_beta, theta_mu=0.0, eps=REF_E
     return -b * float(theta_beta) * np.sign(x) / g * (math.exp(t) + math.exp(-t))
 
 
+# --------------------------------------------------------------------------------------
+# Sandwich relative-position bias (attention-gym "Score Mods", "Sandwich"): the
+# position-position inner product of sinusoidal embeddings, sum_i cos(d w_i) / ratio_h,
+# w_i = 1 / 10000^(2 i / d_bar), ratio_h = 8 (h + 1) / H, no learned parameters.
+# Reading taken: i runs over the d_bar / 2 frequencies of a d_bar-dimensional
+# sinusoidal embedding, i = 0 .. d_bar / 2 - 1.
+# --------------------------------------------------------------------------------------
+
+def sandwich_ratios(H):
+    """ratio_h = 8 (h + 1) / H."""
+    return np.array([8.0 * (h + 1) / H for h in range(H)], np.float64)
+
+
+def prior_bias_sandwich(d, ratio, d_bar=128.0):
+    """b(d) = sum_{i < d_bar/2} cos(d / 10000^(2 i / d_bar)) / ratio."""
+    d = np.asarray(d, np.float64)
+    nf = int(float(d_bar)) // 2
+    out = np.zeros_like(d)
+    for i in range(nf):
+        out += np.cos(d / 10000.0 ** (2.0 * i / float(d_bar)))
+    return out / float(ratio)
+
+
+def _zero_deriv(d, *args):
+    return np.zeros_like(np.asarray(d, np.float64))
+
+
 def _bias_fns(param):
     """(bias, d/dp1, d/dp2, d/dp3) of a parameterisation, each f(d, p1, p2, p3)."""
     if param == "alpha":
@@ -188,6 +217,8 @@ def _bias_fns(param):
     if param == "ref":
         return (prior_bias_ref, prior_bias_ref_dtheta_alpha, prior_bias_ref_dtheta_beta,
                 prior_bias_ref_dtheta_mu)
+    if param == "sandwich":   # alpha = ratio_h, beta = d_bar; no trained parameters
+        return (lambda d, r, db, _m: prior_bias_sandwich(d, r, db), _zero_deriv, _zero_deriv, _zero_deriv)
     raise ValueError(f"unknown parameterisation {param!r}")
 
 

@@ -484,11 +484,29 @@ def check_param_derivatives_fd(orc):
         _close(orc.prior_bias_dmu(dd, alpha, beta, mu), num, 1e-6 * max(1.0, np.max(np.abs(num))), "alpha-form db/dmu FD")
 
 
+
+def check_sandwich_special_cases(orc):
+    """Sandwich bias: d_bar = 2 keeps the single frequency w_0 = 1 (cos d / ratio);
+    d_bar = 4 adds w_1 = 1/100; the value at d = 0 is (d_bar / 2) / ratio; the bias is
+    even in d; the ratios are 8 (h + 1) / H."""
+    d = np.arange(-50, 51)
+    _close(orc.prior_bias_sandwich(d, 2.0, 2.0), np.cos(d) / 2.0, 1e-15, "sandwich d_bar = 2")
+    _close(orc.prior_bias_sandwich(d, 0.5, 4.0), (np.cos(d) + np.cos(d / 100.0)) / 0.5, 1e-13, "sandwich d_bar = 4")
+    _close(orc.prior_bias_sandwich(np.array([0]), 4.0 / 3.0, 128.0), [64.0 * 3.0 / 4.0], 1e-12, "sandwich at d = 0")
+    b = orc.prior_bias_sandwich(d, 1.7, 128.0)
+    _close(b, b[::-1], 1e-12, "sandwich even in d")
+    _close(orc.sandwich_ratios(12), 8.0 * np.arange(1, 13) / 12, 1e-15, "sandwich ratios")
+    # the slowest frequency of d_bar = 128 is 10000^(-126/128): at d = 1 its cosine is
+    # within 1e-7 of 1, so b(0) - b(1) is carried by the fast frequencies alone
+    w = 10000.0 ** (-2.0 * np.arange(64) / 128.0)
+    _close(orc.prior_bias_sandwich(np.array([1]), 1.0, 128.0), [np.sum(np.cos(w))], 1e-12, "sandwich at d = 1")
+
+
 ALL_CHECKS = [
     check_worked_example, check_closed_form_offset_ssmax, check_closed_form_content,
     check_alibi_reduction, check_nope_reduction, check_gaussian_reduction, check_sqrt_reductions,
     check_brute_force, check_invariants, check_weight_ratio_law, check_decode, check_backward_fd,
     check_dalpha_alibi_closed_form, check_special_values,
     check_ref_mu_is_two_sinh, check_ref_reduces_to_alpha_form, check_ref_special_values,
-    check_param_derivatives_fd, check_backward_fd_ref,
+    check_param_derivatives_fd, check_backward_fd_ref, check_sandwich_special_cases,
 ]

@@ -43,6 +43,10 @@ MUTANTS = {
     "ref: chain factor of theta_mu dropped": (" / g * (math.exp(t) + math.exp(-t))", " / g"),
     "ref: dtheta_beta log without eps": ("return prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps) * np.log(g)",
                                          "return prior_bias_ref(d, theta_alpha, theta_beta, theta_mu, eps) * np.log(g - float(eps) + 1e-300)"),
+    "sandwich: frequency exponent i/d_bar": ("np.cos(d / 10000.0 ** (2.0 * i / float(d_bar)))",
+                                             "np.cos(d / 10000.0 ** (1.0 * i / float(d_bar)))"),
+    "sandwich: ratio multiplies": ("return out / float(ratio)", "return out * float(ratio)"),
+    "sandwich: one frequency too many": ("nf = int(float(d_bar)) // 2", "nf = int(float(d_bar)) // 2 + 1"),
     "dmu sign": ("out[nz] = beta * np.power(u[nz], beta) / x[nz]", "out[nz] = -beta * np.power(u[nz], beta) / x[nz]"),
 }
 
