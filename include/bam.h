@@ -88,6 +88,15 @@ typedef int bam_status;
  * beta < 0 precondition does not apply.  Accepted by every entry point. */
 #define BAM_PRIOR_REF 8u
 #define BAM_REF_EPS 1e-5
+/* Sandwich relative-position bias (attention-gym "Score Mods", "Sandwich") in place of the
+ * GGD prior: the inner product of two d_bar-dimensional sinusoidal position embeddings,
+ * scaled down per head,
+ *   b_h(d) = sum_{i = 0}^{d_bar/2 - 1} cos(d / 10000^(2 i / d_bar)) / ratio_h,
+ * with alpha[h] = ratio_h (the page uses 8 (h + 1) / H) and beta[h] = d_bar (the page uses
+ * 128); mu is ignored.  The frequency count is trunc(beta[h]) / 2; above 512 frequencies
+ * the bias is NaN.  The bias has no parameters: the backward's dalpha, dbeta and dmu are
+ * zero.  Not combinable with BAM_PRIOR_REF (BAM_EINVAL).  Accepted by every entry point. */
+#define BAM_PRIOR_SANDWICH 16u
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* bam_status_string(bam_status status);
@@ -114,8 +123,8 @@ bam_status bam_prior_table(const float* alpha, const float* beta, const float* m
 
 /*
  * bam_prior_table_ex - bam_prior_table for either parameterisation, with the offset
- * derivative.  flags: 0 (alpha-form) or BAM_PRIOR_REF.  dalpha, dbeta, dmu may each be
- * NULL.  Alpha-form: dmu = db/dmu = beta u^beta / (d - mu) (0 where u = 0).  Reference
+ * derivative.  flags: 0 (alpha-form), BAM_PRIOR_REF or BAM_PRIOR_SANDWICH (whose
+ * derivatives are zero).  dalpha, dbeta, dmu may each be NULL.  Alpha-form: dmu = db/dmu = beta u^beta / (d - mu) (0 where u = 0).  Reference
  * form, with x = (j - i) - mu and g = |x| + eps:
  *   dalpha = db/dtheta_alpha = b,   dbeta = db/dtheta_beta = b ln g,
  *   dmu    = db/dtheta_mu    = -b theta_beta sign(x) / g * (e^theta_mu + e^-theta_mu)

@@ -14,6 +14,7 @@ import os
 
 __all__ = [
     "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BAM_PRIOR_REF", "BAM_REF_EPS",
+    "BAM_PRIOR_SANDWICH", "sandwich_ratios", "alibi_slopes",
     "BamError", "lib", "lib_path",
     "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_attn_bwd",
@@ -28,6 +29,7 @@ BAM_CAUSAL = 1
 BAM_SSMAX = 2
 BAM_TABLE_READY = 4
 BAM_PRIOR_REF = 8
+BAM_PRIOR_SANDWICH = 16
 BAM_REF_EPS = 1e-5
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -158,8 +160,38 @@ def _workspace(nbytes, device, workspace=None):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def _flags(causal: bool, ssmax: bool, prior_ref: bool = False) -> int:
-    return (BAM_CAUSAL if causal else 0) | (BAM_SSMAX if ssmax else 0) | (BAM_PRIOR_REF if prior_ref else 0)
+_PRIOR_FLAGS = {None: 0, "alpha": 0, "ref": BAM_PRIOR_REF, "sandwich": BAM_PRIOR_SANDWICH}
+
+
+def _prior_flag(prior_ref: bool, prior) -> int:
+    """prior: "alpha" (the GGD alpha-form), "ref" (theta parameterisation) or "sandwich";
+    prior_ref=True is the same as prior="ref"."""
+    if prior not in _PRIOR_FLAGS:
+        raise BamError(f"unknown prior {prior!r}")
+    f = _PRIOR_FLAGS[prior] | (BAM_PRIOR_REF if prior_ref else 0)
+    if f == BAM_PRIOR_REF | BAM_PRIOR_SANDWICH:
+        raise BamError("prior_ref and the sandwich prior exclude each other")
+    return f
+
+
+def _flags(causal: bool, ssmax: bool, prior_ref: bool = False, prior=None) -> int:
+    return (BAM_CAUSAL if causal else 0) | (BAM_SSMAX if ssmax else 0) | _prior_flag(prior_ref, prior)
+
+
+def sandwich_ratios(n_heads, device=None):
+    """Per-head Sandwich compression ratios 8 (h + 1) / H (attention-gym "Score Mods",
+    "Sandwich"), float32 [H]: the alpha argument with prior="sandwich"."""
+    torch = _torch()
+    return torch.tensor([8.0 * (h + 1) / n_heads for h in range(n_heads)], dtype=torch.float32, device=device)
+
+
+def alibi_slopes(n_heads, device=None):
+    """ALiBi slopes 2^(-8 (h + 1) / H), float32 [H] ("ALiBi: Attention with Linear Biases",
+    "Code"; NNX ALiBi-Style Attention, "One fixed slope per head").  ALiBi is the alpha-form
+    prior with beta = 1, mu = 0 and alpha = 1 / slope."""
+    torch = _torch()
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / n_heads) for h in range(n_heads)], dtype=torch.float32,
+                        device=device)
 
 
 # ---------------------------------------------------------------------------------------
@@ -191,27 +223,29 @@ def bam_prior_table(alpha, beta, mu, d0: int, n: int, derivatives: bool = False,
     return (tab, da, db) if derivatives else tab
 
 
-def bam_prior_table_ex(alpha, beta, mu, d0: int, n: int, prior_ref: bool = False, stream=None):
+def bam_prior_table_ex(alpha, beta, mu, d0: int, n: int, prior_ref: bool = False, stream=None, prior=None):
     """(tab, dalpha, dbeta, dmu), each float32 [H, n]: the bias of distance d0 + t and its
     derivatives in the three per-head parameters (theta's with prior_ref)."""
     torch = _torch()
     H = alpha.numel()
     outs = [torch.empty((H, n), dtype=torch.float32, device=alpha.device) for _ in range(4)]
     st = lib().bam_prior_table_ex(_dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), H, d0, n,
-                                  BAM_PRIOR_REF if prior_ref else 0, *(_ptr(t) for t in outs), _stream(stream))
+                                  _prior_flag(prior_ref, prior), *(_ptr(t) for t in outs), _stream(stream))
     _check(st, "bam_prior_table_ex")
     return tuple(outs)
 
 
 def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True, o_dtype=None,
-                 o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False):
+                 o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False,
+                 prior=None):
     """Prefill forward; q, k, v [B, H, T, Dh].  Returns (o, lse).
 
     table_ready: the given workspace already holds this call's distance table (BAM_TABLE_READY).
-    prior_ref: alpha / beta / mu hold theta_alpha / theta_beta / theta_mu (BAM_PRIOR_REF)."""
+    prior_ref: alpha / beta / mu hold theta_alpha / theta_beta / theta_mu (BAM_PRIOR_REF).
+    prior="sandwich": the Sandwich bias, alpha = ratio_h, beta = d_bar (BAM_PRIOR_SANDWICH)."""
     torch = _torch()
     B, H, T, Dh = q.shape
-    flags = _flags(causal, ssmax, prior_ref) | (BAM_TABLE_READY if table_ready else 0)
+    flags = _flags(causal, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(q)
@@ -235,11 +269,12 @@ def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
 
 
 def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, ssmax=True, o_dtype=None,
-                    o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False):
+                    o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False,
+                 prior=None):
     """Decode; q [B, H, Dh], caches [B, H, Lmax, Dh], kv_len int32 [B].  Returns (o, lse)."""
     torch = _torch()
     B, H, Lmax, Dh = k_cache.shape
-    flags = _flags(False, ssmax, prior_ref) | (BAM_TABLE_READY if table_ready else 0)
+    flags = _flags(False, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(k_cache)
@@ -264,13 +299,13 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
 
 def bam_attn_decode_paged(q, k_pages, v_pages, block_table, kv_len, alpha, beta, mu=None, s=None, ssmax=True,
                           o_dtype=None, o=None, lse=None, workspace=None, stream=None, table_ready=False,
-                          prior_ref=False):
+                          prior_ref=False, prior=None):
     """Decode on a paged cache: q [B, H, Dh]; k_pages, v_pages [num_pages, H, page_size, Dh];
     block_table int32 [B, max_blocks]; kv_len int32 [B].  Returns (o, lse)."""
     torch = _torch()
     num_pages, H, page_size, Dh = k_pages.shape
     B, max_blocks = block_table.shape
-    flags = _flags(False, ssmax, prior_ref) | (BAM_TABLE_READY if table_ready else 0)
+    flags = _flags(False, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(k_pages)
@@ -295,24 +330,26 @@ def bam_attn_decode_paged(q, k_pages, v_pages, block_table, kv_len, alpha, beta,
 
 
 def bam_attn_bwd(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
-                 grad_dtype=None, workspace=None, stream=None, prior_ref=False):
+                 grad_dtype=None, workspace=None, stream=None, prior_ref=False,
+                 prior=None):
     """Backward.  Returns (dq, dk, dv, dalpha, dbeta, ds)."""
     return _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream,
-                prior_ref, False)
+                prior_ref, False, prior)
 
 
 def bam_attn_bwd_ex(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
-                    grad_dtype=None, workspace=None, stream=None, prior_ref=False):
+                    grad_dtype=None, workspace=None, stream=None, prior_ref=False,
+                 prior=None):
     """Backward with the offset gradient.  Returns (dq, dk, dv, dalpha, dbeta, dmu, ds)."""
     return _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream,
-                prior_ref, True)
+                prior_ref, True, prior)
 
 
 def _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream, prior_ref,
-         want_mu):
+         want_mu, prior=None):
     torch = _torch()
     B, H, T, Dh = q.shape
-    flags = _flags(causal, ssmax, prior_ref)
+    flags = _flags(causal, ssmax, prior_ref, prior)
     in_code = _dtype_code(q)
     gc = in_code if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
     gdt = _torch_dtype(gc)

@@ -25,28 +25,31 @@ __all__ = ["bam_attention", "BamAttention"]
 
 class _BamAttentionFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, alpha, beta, mu, s, causal, ssmax, prior_ref):
-        o, lse = bam_attn_fwd(q, k, v, alpha, beta, mu, s, causal=causal, ssmax=ssmax, prior_ref=prior_ref)
+    def forward(ctx, q, k, v, alpha, beta, mu, s, causal, ssmax, prior):
+        o, lse = bam_attn_fwd(q, k, v, alpha, beta, mu, s, causal=causal, ssmax=ssmax, prior=prior)
         ctx.save_for_backward(q, k, v, o, lse, alpha, beta, mu, s)
-        ctx.flags = (causal, ssmax, prior_ref)
+        ctx.flags = (causal, ssmax, prior)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, alpha, beta, mu, s = ctx.saved_tensors
-        causal, ssmax, prior_ref = ctx.flags
+        causal, ssmax, prior = ctx.flags
         dq, dk, dv, dalpha, dbeta, dmu, ds = bam_attn_bwd_ex(
-            q, k, v, o, lse, do.contiguous(), alpha, beta, mu, s, causal=causal, ssmax=ssmax,
-            prior_ref=prior_ref)
+            q, k, v, o, lse, do.contiguous(), alpha, beta, mu, s, causal=causal, ssmax=ssmax, prior=prior)
         want = ctx.needs_input_grad
         return (dq if want[0] else None, dk if want[1] else None, dv if want[2] else None,
                 dalpha if want[3] else None, dbeta if want[4] else None, dmu if want[5] else None,
                 ds if (want[6] and ssmax) else None, None, None, None)
 
 
-def bam_attention(q, k, v, alpha, beta, mu, s=None, causal=True, ssmax=True, prior_ref=True):
+def bam_attention(q, k, v, alpha, beta, mu, s=None, causal=True, ssmax=True, prior_ref=True, prior=None):
     """Differentiable BAM attention.  q, k, v: [B, H, T, Dh] (bf16); alpha, beta, mu, s:
-    float32 [H] (theta_alpha, theta_beta, theta_mu with prior_ref).  Returns O [B, H, T, Dh]."""
+    float32 [H] (theta_alpha, theta_beta, theta_mu with prior_ref).  Returns O [B, H, T, Dh].
+    prior: "ref", "alpha" or "sandwich" (alpha = ratio_h, beta = d_bar, no parameter
+    gradients); when given it overrides prior_ref."""
+    if prior is None:
+        prior = "ref" if prior_ref else "alpha"
     if mu is None:
         mu = torch.zeros_like(alpha)
     if s is None:
@@ -54,7 +57,7 @@ def bam_attention(q, k, v, alpha, beta, mu, s=None, causal=True, ssmax=True, pri
             raise ValueError("ssmax needs s")
         s = torch.ones_like(alpha)
     return _BamAttentionFn.apply(q.contiguous(), k.contiguous(), v.contiguous(), alpha, beta, mu, s, causal,
-                                 ssmax, prior_ref)
+                                 ssmax, prior)
 
 
 def _alibi_slopes(n_heads):

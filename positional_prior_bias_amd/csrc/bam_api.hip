@@ -39,8 +39,18 @@ bam_status hip_status(hipError_t e) { return e == hipSuccess ? BAM_OK : BAM_EHIP
 bool prior_ok(const float* alpha, const float* beta, const float* s, unsigned flags) {
   if (alpha == nullptr || beta == nullptr) return false;
   if ((flags & BAM_SSMAX) && s == nullptr) return false;
+  if ((flags & BAM_PRIOR_REF) && (flags & BAM_PRIOR_SANDWICH)) return false;
   return true;
 }
+
+// Table kind selected by the prior flags (at most one is set; prior_ok checks that).
+int prior_kind(unsigned flags) {
+  if (flags & BAM_PRIOR_SANDWICH) return bam::kPriorSandwich;
+  if (flags & BAM_PRIOR_REF) return bam::kPriorRef;
+  return bam::kPriorAlpha;
+}
+
+constexpr unsigned kPriorFlags = BAM_PRIOR_REF | BAM_PRIOR_SANDWICH;
 
 // bf16 forward table: reversed, padded with -inf by kFwdTabPad on each side, sqrt(Dh)-scaled
 // (entry u holds d = dhi + kFwdTabPad - u).  The fp32 path uses the plain table.
@@ -73,7 +83,7 @@ int bam_version(void) { return 100; }
 bam_status bam_prior_table(const float* alpha, const float* beta, const float* mu, int H, int d0,
                            int n, float* tab, float* dalpha, float* dbeta, void* stream) {
   if (alpha == nullptr || beta == nullptr || tab == nullptr || H <= 0 || n <= 0) return BAM_EINVAL;
-  return hip_status(bam::launch_prior_table(alpha, beta, mu, false, H, d0, n, n, 1.0f, tab, dalpha, dbeta,
+  return hip_status(bam::launch_prior_table(alpha, beta, mu, bam::kPriorAlpha, H, d0, n, n, 1.0f, tab, dalpha, dbeta,
                                             nullptr, (hipStream_t)stream));
 }
 
@@ -81,8 +91,8 @@ bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float
                               int n, unsigned flags, float* tab, float* dalpha, float* dbeta, float* dmu,
                               void* stream) {
   if (alpha == nullptr || beta == nullptr || tab == nullptr || H <= 0 || n <= 0) return BAM_EINVAL;
-  if ((flags & ~BAM_PRIOR_REF) != 0) return BAM_EINVAL;
-  return hip_status(bam::launch_prior_table(alpha, beta, mu, (flags & BAM_PRIOR_REF) != 0, H, d0, n, n, 1.0f,
+  if ((flags & ~kPriorFlags) != 0 || !prior_ok(alpha, beta, nullptr, flags)) return BAM_EINVAL;
+  return hip_status(bam::launch_prior_table(alpha, beta, mu, prior_kind(flags), H, d0, n, n, 1.0f,
                                             tab, dalpha, dbeta, dmu, (hipStream_t)stream));
 }
 
@@ -103,7 +113,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       lse == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | kPriorFlags)) != 0) return BAM_EINVAL;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   if (in_dtype == BAM_BF16) {
     if (Dh != 32 && Dh != 64 && Dh != 128) return BAM_EUNSUPPORTED;
@@ -116,7 +126,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (workspace_bytes < bam_fwd_workspace_size(B, H, T, Dh, flags)) return BAM_EWORKSPACE;
 
   const bool causal = (flags & BAM_CAUSAL) != 0;
-  const bool ref = (flags & BAM_PRIOR_REF) != 0;
+  const int kind = prior_kind(flags);
   const bool bf16 = in_dtype == BAM_BF16;
   const TableGeom g = bf16 ? fwd_table_geom(T, causal) : table_geom(T, causal);
   hipStream_t st = (hipStream_t)stream;
@@ -124,10 +134,10 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   hipError_t e = hipSuccess;
   if (!(flags & BAM_TABLE_READY)) {
     if (bf16)
-      e = bam::launch_prior_table_ex(alpha, beta, mu, ref, H, g.d0, -1, g.n, g.stride, causal ? 0 : -(T - 1), T - 1,
+      e = bam::launch_prior_table_ex(alpha, beta, mu, kind, H, g.d0, -1, g.n, g.stride, causal ? 0 : -(T - 1), T - 1,
                                      std::sqrt((float)Dh), tab, nullptr, nullptr, nullptr, st);
     else
-      e = bam::launch_prior_table(alpha, beta, mu, ref, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr,
+      e = bam::launch_prior_table(alpha, beta, mu, kind, H, g.d0, g.n, g.stride, 1.0f, tab, nullptr, nullptr,
                                   nullptr, st);
     if (e != hipSuccess) return BAM_EHIP;
   }
@@ -184,7 +194,7 @@ bam_status decode_common(const void* q, const void* k, const void* v, int in_dty
   if (!dims_ok(B, H, Lmax) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       lse == nullptr || kv_len == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | kPriorFlags)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   const DecodeLayout L = decode_layout(B, H, Lmax, Dh);
@@ -192,7 +202,7 @@ bam_status decode_common(const void* q, const void* k, const void* v, int in_dty
   hipStream_t st = (hipStream_t)stream;
   float* tab = (float*)((char*)workspace + L.tab_off);
   if (!(flags & BAM_TABLE_READY)) {
-    hipError_t e = bam::launch_prior_table(alpha, beta, mu, (flags & BAM_PRIOR_REF) != 0, H, 0, Lmax, L.tab_stride,
+    hipError_t e = bam::launch_prior_table(alpha, beta, mu, prior_kind(flags), H, 0, Lmax, L.tab_stride,
                                            1.0f, tab, nullptr, nullptr, nullptr, st);
     if (e != hipSuccess) return BAM_EHIP;
   }
@@ -294,7 +304,7 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
       dalpha == nullptr || dbeta == nullptr || ds == nullptr || workspace == nullptr ||
       !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_PRIOR_REF)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | kPriorFlags)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64)) return BAM_EUNSUPPORTED;
   if ((o_dtype != BAM_BF16 && o_dtype != BAM_F32) || (grad_dtype != BAM_BF16 && grad_dtype != BAM_F32))
     return BAM_EUNSUPPORTED;
@@ -307,7 +317,7 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   float* ta = (float*)(ws + L.ta_off);
   float* tb = (float*)(ws + L.tb_off);
   float* tm = dmu ? (float*)(ws + L.tm_off) : nullptr;
-  hipError_t e = bam::launch_prior_table(alpha, beta, mu, (flags & BAM_PRIOR_REF) != 0, H, L.g.d0, L.g.n,
+  hipError_t e = bam::launch_prior_table(alpha, beta, mu, prior_kind(flags), H, L.g.d0, L.g.n,
                                          L.g.stride, 1.0f, tab, ta, tb, tm, st);
   if (e != hipSuccess) return BAM_EHIP;
   bam::BwdArgs a;

@@ -7,14 +7,21 @@
 
 namespace bam {
 
+// Which per-head function of the distance the table holds.
+enum PriorKind : int {
+  kPriorAlpha = 0,     // -|(d - mu) / alpha|^beta
+  kPriorRef = 1,       // -e^theta_alpha (|(j - i) - mu| + eps)^theta_beta
+  kPriorSandwich = 2,  // sum_i cos(d w_i) / ratio (alpha = ratio, beta = d_bar)
+};
+
 // Launch the distance-table kernel: tab[h*stride + t] = b_h(d0 + t) (and derivatives;
-// any derivative pointer may be null).  ref: reference parameterisation (theta's).
-hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, bool ref, int H,
+// any derivative pointer may be null).
+hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int kind, int H,
                               int d0, int n, int stride, float scale, float* tab, float* dalpha,
                               float* dbeta, float* dmu, hipStream_t stream);
 // General form: entry t holds d = d_first + step * t; entries with d outside [dlo, dhi]
 // are padding (-inf bias, zero derivatives).  The bias is multiplied by `scale`.
-hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, bool ref, int H,
+hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, int kind, int H,
                                  int d_first, int step, int n, int stride, int dlo, int dhi, float scale,
                                  float* tab, float* dalpha, float* dbeta, float* dmu, hipStream_t stream);
 

@@ -7,6 +7,11 @@
 // alpha and beta are trained parameters ("Bayesian Attention Mechanism",
 // "Implementation Details").  One pow per (head, distance), evaluated in float64 and
 // rounded once to float32.
+//
+// The same table carries any other bias that depends on the head and i - j only.  The
+// Sandwich bias (attention-gym "Score Mods", "Sandwich") is the inner product of two
+// d_bar-dimensional sinusoidal position embeddings, sum_i cos(d w_i) / ratio_h with
+// w_i = 10000^(-2 i / d_bar) over the d_bar / 2 frequencies, and has no parameters.
 #include "../../include/bam.h"
 #include "bam_device.h"
 #include "bam_internal.h"
@@ -15,13 +20,18 @@ namespace bam {
 
 // Entry t of head h holds distance d = d_first + step * t.  Distances outside
 // [dlo, dhi] are padding: -inf in the bias table (a key never visible), 0 in the
-// derivative tables.  ref = 0: alpha-form; ref = 1: the reference parameterisation
-// ("Bayesian Attention Mechanism", "Implementation Details"), where alpha / beta / mu
-// hold theta_alpha / theta_beta / theta_mu, x = (j - i) - mu = -d - mu,
-// mu = e^theta_mu - e^-theta_mu and b = -e^theta_alpha (|x| + eps)^theta_beta.
+// derivative tables.  kind kPriorAlpha: alpha-form; kPriorRef: the reference
+// parameterisation ("Bayesian Attention Mechanism", "Implementation Details"), where
+// alpha / beta / mu hold theta_alpha / theta_beta / theta_mu, x = (j - i) - mu = -d - mu,
+// mu = e^theta_mu - e^-theta_mu and b = -e^theta_alpha (|x| + eps)^theta_beta;
+// kPriorSandwich: alpha holds ratio_h and beta d_bar (the frequency count is
+// trunc(d_bar) / 2, at most kSandwichMaxFreq; beyond that the entries are NaN), and the
+// derivative tables are zero.
+constexpr int kSandwichMaxFreq = 512;
+
 __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restrict__ alpha,
                                                           const float* __restrict__ beta,
-                                                          const float* __restrict__ mu, int ref,
+                                                          const float* __restrict__ mu, int kind,
                                                           int d_first, int step, int n, int stride,
                                                           int dlo, int dhi, float scale,
                                                           float* __restrict__ tab,
@@ -30,6 +40,15 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
                                                           float* __restrict__ tm) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
+  // Sandwich: the inverse frequencies 10000^(2 i / d_bar) of this head, once per block.
+  __shared__ double inv_w[kSandwichMaxFreq];
+  int nf = 0;
+  if (kind == kPriorSandwich) {
+    nf = (int)beta[h] / 2;
+    for (int i = threadIdx.x; i < kSandwichMaxFreq && i < nf; i += blockDim.x)
+      inv_w[i] = pow(10000.0, 2.0 * i / (double)beta[h]);
+    __syncthreads();
+  }
   if (t >= n) return;
   const int d = d_first + step * t;
   const size_t idx = (size_t)h * stride + t;
@@ -44,7 +63,15 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   const double be = beta[h];
   const double m = mu ? (double)mu[h] : 0.0;
   double b, da = 0.0, db = 0.0, dm = 0.0;
-  if (ref) {
+  if (kind == kPriorSandwich) {
+    if (nf > kSandwichMaxFreq) {
+      b = __builtin_nan("");
+    } else {
+      double acc = 0.0;
+      for (int i = 0; i < nf; ++i) acc += cos((double)d / inv_w[i]);
+      b = acc / a;
+    }
+  } else if (kind == kPriorRef) {
     // b = -e^ta g^tb, g = |x| + eps: db/dta = b, db/dtb = b ln g,
     // db/dtm = -b tb sign(x) / g * (e^tm + e^-tm)
     const double em = exp(m), emi = exp(-m);
@@ -77,18 +104,18 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   if (tm) tm[idx] = (float)dm;
 }
 
-hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, bool ref, int H,
+hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int kind, int H,
                               int d0, int n, int stride, float scale, float* tab, float* dalpha,
                               float* dbeta, float* dmu, hipStream_t stream) {
-  return launch_prior_table_ex(alpha, beta, mu, ref, H, d0, 1, n, stride, d0, d0 + n - 1, scale, tab,
+  return launch_prior_table_ex(alpha, beta, mu, kind, H, d0, 1, n, stride, d0, d0 + n - 1, scale, tab,
                                dalpha, dbeta, dmu, stream);
 }
 
-hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, bool ref, int H,
+hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const float* mu, int kind, int H,
                                  int d_first, int step, int n, int stride, int dlo, int dhi, float scale,
                                  float* tab, float* dalpha, float* dbeta, float* dmu, hipStream_t stream) {
   dim3 grid((n + 255) / 256, H);
-  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), 0, stream, alpha, beta, mu, ref ? 1 : 0, d_first,
+  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), 0, stream, alpha, beta, mu, kind, d_first,
                      step, n, stride, dlo, dhi, scale, tab, dalpha, dbeta, dmu);
   return hipGetLastError();
 }

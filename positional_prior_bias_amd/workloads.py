@@ -243,6 +243,26 @@ def ref_case(seed: int, B: int, H: int, T: int, Dh: int, dtype: str = "bf16", fl
     return w
 
 
+def sandwich_case(seed: int, B: int, H: int, T: int, Dh: int, dtype: str = "bf16", flags: int = CAUSAL | SSMAX,
+                  d_bar: float = 128.0, s_range=(0.3, 0.6), with_grad: bool = False) -> Workload:
+    """Small case with the Sandwich bias: alpha holds the per-head compression ratios
+    8 (h + 1) / H and beta d_bar (attention-gym "Score Mods", "Sandwich": the page's
+    defaults); mu is zero.  Draw order: Q, K, V, s ~ U, then dO if requested.
+    """
+    rng = np.random.default_rng(seed)
+    bf = dtype == "bf16"
+    q = _normal(rng, (B, H, T, Dh), bf)
+    k = _normal(rng, (B, H, T, Dh), bf)
+    v = _normal(rng, (B, H, T, Dh), bf)
+    ratio = np.array([8.0 * (h + 1) / H for h in range(H)], np.float32)
+    dbar = np.full(H, d_bar, np.float32)
+    s = rng.uniform(s_range[0], s_range[1], H).astype(np.float32)
+    w = Workload("sandwich_T%d" % T, B, H, T, Dh, dtype, flags, ratio, dbar, np.zeros(H, np.float32), s, q, k, v)
+    if with_grad:
+        w.do = _normal(rng, (B, H, T, Dh), bf)
+    return w
+
+
 def alibi_slopes(H: int) -> np.ndarray:
     """Per-head ALiBi slopes m_h = 2^(-8(h+1)/H) for every H.
 
