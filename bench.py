@@ -123,6 +123,42 @@ def bench_fwd(torch, bam, w, steps, warmup, timer, name):
                 kernel_gbs=algo_bytes / kern_ms / 1e6)
 
 
+def bench_skip(torch, bam, w, steps, timer):
+    """Prior-aware key skipping (BAM_SKIP_FAR) on the 32k prefill: the forward call with and
+    without it, table prebuilt in both (the skipping plan's kernels are inside the timed
+    call).  Two prior settings: the workload's own heads, and the pages' AttentionPrior
+    initialisation in the reference form (theta_alpha = ALiBi slopes, theta_beta =
+    linspace(0, 1), theta_mu = 0, s = 1 / ln 512).  Skipping changes the work, not the
+    result, so these figures are kept apart from the algorithmic-flop metric."""
+    x = device_inputs(torch, w)
+    B, H, T, Dh = w.q.shape
+    o = torch.empty((B, H, T, Dh), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    slopes = bam.alibi_slopes(H, device="cuda")
+    init = dict(alpha=slopes, beta=torch.linspace(0, 1, H, dtype=torch.float32, device="cuda"),
+                mu=torch.zeros(H, dtype=torch.float32, device="cuda"),
+                s=torch.full((H,), 1.0 / math.log(512.0), dtype=torch.float32, device="cuda"))
+    out = {}
+    for name, p, ref in (("workload_heads", x, False), ("pages_init_ref_form", init, True)):
+        flags = bam.BAM_CAUSAL | bam.BAM_SSMAX | bam.BAM_SKIP_FAR | (bam.BAM_PRIOR_REF if ref else 0)
+        ws = torch.empty(bam.bam_fwd_workspace_size(B, H, T, Dh, flags), dtype=torch.uint8, device="cuda")
+
+        def call(skip, table_ready=True):
+            bam.bam_attn_fwd(x["q"], x["k"], x["v"], p["alpha"], p["beta"], p["mu"], p["s"], causal=True,
+                             ssmax=True, o=o, lse=lse, workspace=ws, table_ready=table_ready, prior_ref=ref,
+                             skip_far=skip)
+        call(True, table_ready=False)
+        frac = bam.fwd_skipped_fraction(ws, B, H, T, Dh, flags)
+        full = timer.per_launch(lambda: call(False), steps)
+        skip = timer.per_launch(lambda: call(True), steps)
+        flops = fwd_flops(B, H, T, Dh)
+        log(f"[skip32k:{name}] full {full:.4f} ms, skipping {skip:.4f} ms, skipped fraction {frac:.3f}")
+        out[name] = {"skipped_tile_fraction": round(frac, 4), "full_ms": round(full, 4), "skip_ms": round(skip, 4),
+                     "speedup": round(full / skip, 3),
+                     "effective_TFLOP/s": round(flops / skip / 1e9, 1)}
+    return out
+
+
 def bench_fwdbwd(torch, bam, w, steps, warmup, timer):
     x = device_inputs(torch, w, with_grad=True)
     B, H, T, Dh = w.q.shape
@@ -255,9 +291,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--parts", default="fwd512,fwd32k,decode,fwdbwd512,train512",
-                    help="comma list of fwd512,fwd32k,decode,fwdbwd512,train512,sweep (fwd512 is always "
-                         "run; sweep, the length sweep, is not run by default)")
+    ap.add_argument("--parts", default="fwd512,fwd32k,skip32k,decode,fwdbwd512,train512",
+                    help="comma list of fwd512,fwd32k,skip32k,decode,fwdbwd512,train512,sweep (fwd512 is "
+                         "always run; skip32k needs fwd32k; sweep, the length sweep, is not run by default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -306,6 +342,11 @@ def main():
             "kernel_pct_mfma_peak": round(100 * r["kernel_tflops"] / PEAK_BF16_TFLOPS, 2),
             "roofline": {"bound": "mfma", "achieved": round(r["kernel_tflops"], 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)}}
+        if "skip32k" in parts:
+            out_parts["skip_T32768"] = {
+                "note": "prior-aware key skipping: same results, less work; effective_TFLOP/s = the dense "
+                        "algorithmic flops / the skipping call's time, not the metric",
+                **bench_skip(torch, bam, w4, max(3, args.steps // 4), timer)}
         del w4
     if "decode" in parts:
         log("[decode] generating inputs (256,000-token caches)")

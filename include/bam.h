@@ -97,6 +97,18 @@ typedef int bam_status;
  * the bias is NaN.  The bias has no parameters: the backward's dalpha, dbeta and dmu are
  * zero.  Not combinable with BAM_PRIOR_REF (BAM_EINVAL).  Accepted by every entry point. */
 #define BAM_PRIOR_SANDWICH 16u
+/* Prior-aware key skipping (bam_attn_fwd, causal bf16 only; BAM_EUNSUPPORTED otherwise).
+ * For each block of query rows the call first bounds every logit from above,
+ *   l_ij <= c_i (|q_i| max_j |k_j| / sqrt(Dh) + max_{d >= i - j} b(d)),
+ * and the row maximum from below by the diagonal logit l_ii, then leaves out the leading
+ * 64-key tiles whose every key sits more than 104 (> 150 ln 2) below that lower bound for
+ * every row of the block.  Such a key's softmax weight is below 2^-150 of its row's
+ * largest, i.e. zero in float32: the result is that of the full computation at float32
+ * precision, while a prior that decays with distance (beta > 0 local heads) saves the far
+ * tiles.  Rows with c_i <= 0 and non-finite bounds never skip; the bound assumes finite
+ * q, k and bias.  Needs the larger workspace that bam_fwd_workspace_size reports for
+ * these flags. */
+#define BAM_SKIP_FAR 32u
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* bam_status_string(bam_status status);
@@ -142,7 +154,7 @@ bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float
  * o: [B, H, T, Dh] of o_dtype (BAM_BF16 output is the round-to-nearest-even of the
  * float32 result).  lse: [B, H, T] float32, natural log.
  * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128} (bf16 MFMA, fp32 accumulate);
- * in_dtype BAM_F32 with Dh in {32, 64} (fp32 throughout).
+ * in_dtype BAM_F32 with Dh in {32, 64} (fp32 throughout).  BAM_SKIP_FAR: see above.
  */
 size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
 bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtype,
@@ -150,6 +162,19 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
                         const float* alpha, const float* beta, const float* mu, const float* s,
                         unsigned flags, void* o, int o_dtype, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bam_fwd_skip_plan_offset - where a BAM_SKIP_FAR forward leaves its skipping plan.
+ *
+ * After bam_attn_fwd with these flags (which must include BAM_CAUSAL | BAM_SKIP_FAR), the
+ * workspace holds, at byte *offset, *count = ceil(T / R) * B * H int32 values, R = 256
+ * query rows per block for Dh <= 64 and 128 for Dh = 128.  Entry qb * B * H + b * H + h
+ * is the number of leading 64-key tiles that query block qb of (b, h) left out.  For
+ * measuring how much work the prior saved; the plan is rewritten by every such call.
+ * Returns BAM_EUNSUPPORTED for flags without BAM_CAUSAL | BAM_SKIP_FAR or an unsupported Dh.
+ */
+bam_status bam_fwd_skip_plan_offset(int B, int H, int T, int Dh, unsigned flags, size_t* offset,
+                                    int* count);
 
 /*
  * bam_attn_decode - one new query row per sequence against a KV cache (split-KV).

@@ -14,7 +14,8 @@ import os
 
 __all__ = [
     "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BAM_PRIOR_REF", "BAM_REF_EPS",
-    "BAM_PRIOR_SANDWICH", "sandwich_ratios", "alibi_slopes",
+    "BAM_PRIOR_SANDWICH", "sandwich_ratios", "alibi_slopes", "BAM_SKIP_FAR", "bam_fwd_skip_plan_offset",
+    "fwd_skipped_fraction",
     "BamError", "lib", "lib_path",
     "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_attn_bwd",
@@ -30,6 +31,7 @@ BAM_SSMAX = 2
 BAM_TABLE_READY = 4
 BAM_PRIOR_REF = 8
 BAM_PRIOR_SANDWICH = 16
+BAM_SKIP_FAR = 32
 BAM_REF_EPS = 1e-5
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +39,7 @@ _LIB = None
 
 EXPORTED_SYMBOLS = (
     "bam_status_string", "bam_version", "bam_prior_table", "bam_prior_table_ex",
-    "bam_fwd_workspace_size", "bam_attn_fwd",
+    "bam_fwd_workspace_size", "bam_attn_fwd", "bam_fwd_skip_plan_offset",
     "bam_decode_workspace_size", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_bwd_workspace_size", "bam_attn_bwd", "bam_attn_bwd_ex",
 )
@@ -64,6 +66,8 @@ def _declare(L):
     L.bam_fwd_workspace_size.restype = sz
     L.bam_fwd_workspace_size.argtypes = [i, i, i, i, u]
     L.bam_attn_fwd.restype = i
+    L.bam_fwd_skip_plan_offset.restype = i
+    L.bam_fwd_skip_plan_offset.argtypes = [i, i, i, i, u, ctypes.POINTER(sz), ctypes.POINTER(i)]
     L.bam_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp, sz, vp]
     L.bam_decode_workspace_size.restype = sz
     L.bam_decode_workspace_size.argtypes = [i, i, i, i]
@@ -235,17 +239,42 @@ def bam_prior_table_ex(alpha, beta, mu, d0: int, n: int, prior_ref: bool = False
     return tuple(outs)
 
 
+def bam_fwd_skip_plan_offset(B, H, T, Dh, flags):
+    """(byte offset, count) of the int32 skipping plan a BAM_SKIP_FAR forward leaves in its
+    workspace: entry qb * B * H + b * H + h = leading 64-key tiles query block qb skipped."""
+    off, cnt = ctypes.c_size_t(0), ctypes.c_int(0)
+    _check(lib().bam_fwd_skip_plan_offset(B, H, T, Dh, flags, ctypes.byref(off), ctypes.byref(cnt)),
+           "bam_fwd_skip_plan_offset")
+    return int(off.value), int(cnt.value)
+
+
+def fwd_skipped_fraction(workspace, B, H, T, Dh, flags):
+    """Fraction of the causal forward's (query block, key tile) pairs that the last
+    BAM_SKIP_FAR call on `workspace` left out (reads the plan back to the host)."""
+    torch = _torch()
+    off, cnt = bam_fwd_skip_plan_offset(B, H, T, Dh, flags)
+    plan = workspace[off:off + 4 * cnt].view(torch.int32).cpu().long()
+    rows = 256 if Dh <= 64 else 128
+    nqb = cnt // (B * H)
+    qb = torch.arange(nqb).repeat_interleave(B * H)
+    total = ((torch.clamp((qb + 1) * rows, max=T) + 63) // 64).sum().item()
+    return float(plan.sum().item()) / float(total)
+
+
 def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True, o_dtype=None,
                  o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False,
-                 prior=None):
+                 prior=None, skip_far=False):
     """Prefill forward; q, k, v [B, H, T, Dh].  Returns (o, lse).
 
     table_ready: the given workspace already holds this call's distance table (BAM_TABLE_READY).
     prior_ref: alpha / beta / mu hold theta_alpha / theta_beta / theta_mu (BAM_PRIOR_REF).
-    prior="sandwich": the Sandwich bias, alpha = ratio_h, beta = d_bar (BAM_PRIOR_SANDWICH)."""
+    prior="sandwich": the Sandwich bias, alpha = ratio_h, beta = d_bar (BAM_PRIOR_SANDWICH).
+    skip_far: leave out the leading key tiles whose weights are zero in float32 (BAM_SKIP_FAR;
+    causal bf16 only)."""
     torch = _torch()
     B, H, T, Dh = q.shape
-    flags = _flags(causal, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
+    flags = (_flags(causal, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
+             | (BAM_SKIP_FAR if skip_far else 0))
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(q)

@@ -63,6 +63,31 @@ TableGeom fwd_table_geom(int T, bool causal) {
   return r;
 }
 
+// Forward workspace: the distance table, then (BAM_SKIP_FAR) the skipping plan's arrays.
+struct FwdLayout {
+  size_t smax_off, rowu_off, rowv_off, kpart_off, first_off, total;
+  int nqb, nparts;
+};
+
+FwdLayout fwd_layout(int B, int H, int T, int Dh, unsigned flags) {
+  FwdLayout L{};
+  const bool causal = (flags & BAM_CAUSAL) != 0;
+  const TableGeom g = fwd_table_geom(T, causal);
+  L.total = align_up((size_t)H * g.stride * sizeof(float));
+  if ((flags & BAM_SKIP_FAR) && causal && Dh > 0 && Dh % 8 == 0 && Dh <= 128) {
+    const size_t BH = (size_t)B * H;
+    L.nqb = (T + bam::fwd_bf16_rows_per_block(Dh) - 1) / bam::fwd_bf16_rows_per_block(Dh);
+    L.nparts = (T + bam::skip_rows_per_block(Dh) - 1) / bam::skip_rows_per_block(Dh);
+    L.smax_off = L.total;
+    L.rowu_off = L.smax_off + align_up((size_t)H * T * sizeof(float));
+    L.rowv_off = L.rowu_off + align_up(BH * T * sizeof(float));
+    L.kpart_off = L.rowv_off + align_up(BH * T * sizeof(float));
+    L.first_off = L.kpart_off + align_up(BH * L.nparts * sizeof(float));
+    L.total = L.first_off + align_up(BH * L.nqb * sizeof(int32_t));
+  }
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,12 +123,19 @@ bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float
 
 // ---------------------------------------------------------------------------------------
 size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags) {
-  (void)B;
-  (void)Dh;
   if (H <= 0 || T <= 0) return 0;
-  const bool causal = (flags & BAM_CAUSAL) != 0;
-  const TableGeom g = fwd_table_geom(T, causal);
-  return align_up((size_t)H * g.stride * sizeof(float));
+  return fwd_layout(B, H, T, Dh, flags).total;
+}
+
+bam_status bam_fwd_skip_plan_offset(int B, int H, int T, int Dh, unsigned flags, size_t* offset,
+                                    int* count) {
+  if (!dims_ok(B, H, T) || offset == nullptr || count == nullptr) return BAM_EINVAL;
+  if (!(flags & BAM_SKIP_FAR) || !(flags & BAM_CAUSAL) || (Dh != 32 && Dh != 64 && Dh != 128))
+    return BAM_EUNSUPPORTED;
+  const FwdLayout L = fwd_layout(B, H, T, Dh, flags);
+  *offset = L.first_off;
+  *count = L.nqb * B * H;
+  return BAM_OK;
 }
 
 bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtype, int B, int H, int T,
@@ -113,8 +145,9 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   if (!dims_ok(B, H, T) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       lse == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | kPriorFlags)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | kPriorFlags | BAM_SKIP_FAR)) != 0) return BAM_EINVAL;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
+  if ((flags & BAM_SKIP_FAR) && (in_dtype != BAM_BF16 || !(flags & BAM_CAUSAL))) return BAM_EUNSUPPORTED;
   if (in_dtype == BAM_BF16) {
     if (Dh != 32 && Dh != 64 && Dh != 128) return BAM_EUNSUPPORTED;
   } else if (in_dtype == BAM_F32) {
@@ -157,6 +190,27 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   a.o = o;
   a.o_f32 = o_dtype == BAM_F32;
   a.lse = lse;
+  a.first_tile = nullptr;
+  if (flags & BAM_SKIP_FAR) {
+    const FwdLayout L = fwd_layout(B, H, T, Dh, flags);
+    char* ws = (char*)workspace;
+    bam::SkipArgs sk;
+    sk.q = q;
+    sk.k = k;
+    sk.tab = tab;
+    sk.tab_d0 = g.d0;
+    sk.tab_stride = g.stride;
+    sk.s = s;
+    sk.ssmax = a.ssmax;
+    sk.smax = (float*)(ws + L.smax_off);
+    sk.rowu = (float*)(ws + L.rowu_off);
+    sk.rowv = (float*)(ws + L.rowv_off);
+    sk.kpart = (float*)(ws + L.kpart_off);
+    sk.first_tile = (int32_t*)(ws + L.first_off);
+    e = bam::launch_fwd_skip_plan(sk, B, H, T, Dh, bam::fwd_bf16_rows_per_block(Dh), st);
+    if (e != hipSuccess) return BAM_EHIP;
+    a.first_tile = sk.first_tile;
+  }
   e = bf16 ? bam::launch_fwd_bf16(a, Dh, st) : bam::launch_fwd_f32(a, Dh, st);
   return hip_status(e);
 }

@@ -43,9 +43,32 @@ struct FwdArgs {
   void* o;
   bool o_f32;
   float* lse;
+  const int32_t* first_tile;   // per work-group first key tile (prior-aware skipping), or null
 };
 
+// Query rows per work-group of the bf16 forward kernel.
+constexpr int fwd_bf16_rows_per_block(int Dh) { return Dh <= 64 ? 256 : 128; }
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, int Dh, hipStream_t stream);
+
+// Prior-aware skipping plan (causal bf16 forward): inputs and the workspace arrays it fills.
+struct SkipArgs {
+  const void* q;          // [B,H,T,Dh] bf16
+  const void* k;
+  const float* tab;       // the forward's reversed sqrt(Dh)-scaled table
+  int tab_d0;             // its entry holding d = 0
+  int tab_stride;
+  const float* s;         // SSMax strength (null without SSMax)
+  bool ssmax;
+  float* smax;            // [H][T] suffix maximum of the bias over distances
+  float* rowu;            // [B*H][T]
+  float* rowv;            // [B*H][T]
+  float* kpart;           // [B*H][nparts] per-block max |k|
+  int32_t* first_tile;    // [nqb * B * H]
+};
+
+int skip_rows_per_block(int Dh);
+hipError_t launch_fwd_skip_plan(const SkipArgs& a, int B, int H, int T, int Dh, int MQ, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int Dh, hipStream_t stream);
 
 struct DecodeArgs {

@@ -30,6 +30,8 @@
 //     lse is within 2^-11 of the fp32 value.
 //   * K / V rows in LDS have their 16-byte chunks XOR-swizzled by row so operand reads do
 //     not collide in banks.
+//   * With a skipping plan (causal only), a work-group starts its key loop at the first
+//     key tile whose weights float32 can still hold (the bound is in skip.hip).
 #include <float.h>
 
 #include "bam_device.h"
@@ -123,7 +125,12 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
       for (int x = 0; x < 16; ++x) oacc[qb2][db][x] = 0.f;
 
   const int kend = CAUSAL ? min(T, i0 + MQ) : T;
-  const int ntiles = (kend + kNK - 1) / kNK;
+  // key tiles before tf carry no weight float32 can hold (prior-aware plan; causal only)
+  int tf = 0;
+  if (CAUSAL && a.first_tile)
+    tf = min(max(__builtin_amdgcn_readfirstlane(a.first_tile[qb * BH + bh]), 0), i0 / kNK);
+  const int jb = tf * kNK;                          // first key of the loop
+  const int ntiles = (kend - jb + kNK - 1) / kNK;   // tiles from jb on
   const float* tabh = a.tab + (size_t)h * a.tab_stride;
 
   // window value index y of this lane's first accumulator group; the four values of each
@@ -199,7 +206,7 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   };
 
   auto compute_tile = [&](const FwdTile<DH, TW>& tl, FwdTile<DH, TW>& nx, int t) {
-    const int j0 = t * kNK;
+    const int j0 = jb + t * kNK;
     // a wave whose rows all precede this tile's keys has nothing to do (causal)
     if (CAUSAL && j0 > iw + QW - 1) {
       convert_next(nx, t);
@@ -338,9 +345,9 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   // in registers before the first tile load is issued (the compiler would otherwise wait
   // for it, and so for every load in flight, inside the loop).
   BAM_WAIT_VMCNT(0);
-  issue_tile(tA, 0);
+  issue_tile(tA, jb);
   if (ntiles > 1) {
-    issue_tile(tB, kNK);
+    issue_tile(tB, jb + kNK);
     BAM_WAIT_VMCNT(LPT);       // this wave's loads of tile 0 landed (tile 1 may be in flight)
   } else {
     BAM_WAIT_VMCNT(0);
@@ -350,15 +357,15 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   // every wave has waited for its loads of tile t + 1 (in compute_tile); publish it
   auto advance = [&]() { BAM_BARRIER_VMCNT(63); };
   for (int t = 0; t < ntiles; t += 3) {
-    if (t + 2 < ntiles) issue_tile(tC, (t + 2) * kNK);
+    if (t + 2 < ntiles) issue_tile(tC, jb + (t + 2) * kNK);
     compute_tile(tA, tB, t);
     advance();
     if (t + 1 >= ntiles) break;
-    if (t + 3 < ntiles) issue_tile(tA, (t + 3) * kNK);
+    if (t + 3 < ntiles) issue_tile(tA, jb + (t + 3) * kNK);
     compute_tile(tB, tC, t + 1);
     advance();
     if (t + 2 >= ntiles) break;
-    if (t + 4 < ntiles) issue_tile(tB, (t + 4) * kNK);
+    if (t + 4 < ntiles) issue_tile(tB, jb + (t + 4) * kNK);
     compute_tile(tC, tA, t + 2);
     advance();
   }
@@ -507,6 +514,7 @@ template <int DH, bool CAUSAL>
 hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int NQB = DH <= 64 ? 2 : 1;
   constexpr int MQ = 4 * 32 * NQB;
+  static_assert(MQ == fwd_bf16_rows_per_block(DH), "rows per work-group");
   const int nqb = (a.T + MQ - 1) / MQ;
   const long nblocks = (long)nqb * a.B * a.H;
   hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL, NQB>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, nqb);

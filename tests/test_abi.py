@@ -84,7 +84,8 @@ def test_fwd_rejects_bad_arguments_before_launch(L):
     assert _fwd(L, q=None) == 1
     assert _fwd(L, q=8) == 1                      # misaligned
     assert _fwd(L, T=0) == 1
-    assert _fwd(L, flags=32) == 1                 # unknown flag bit
+    assert _fwd(L, flags=64) == 1                 # unknown flag bit
+    assert _fwd(L, flags=2 | 32) == 2             # skipping needs the causal bf16 path
     assert _fwd(L, flags=3 | 8 | 16) == 1         # two prior kinds at once
     assert _fwd(L, s=None) == 1                   # SSMax without s
     assert _fwd(L, Dh=48) == 2
@@ -112,7 +113,7 @@ def test_decode_and_bwd_reject_bad_arguments(L):
     st = L.bam_attn_bwd_ex(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 64, 16, 16, None, 16, 3 | 8, 16, 16, 16, 0,
                            None, 16, 16, 16, 256, 1 << 20, None)
     assert st == 1                                 # dalpha NULL (extended backward)
-    st = L.bam_attn_bwd_ex(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 64, 16, 16, None, 16, 32 | 3, 16, 16, 16, 0,
+    st = L.bam_attn_bwd_ex(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 64, 16, 16, None, 16, 64 | 3, 16, 16, 16, 0,
                            16, 16, 16, 16, 256, 1 << 20, None)
     assert st == 1                                 # unknown flag bit
     assert L.bam_prior_table_ex(16, 16, None, 1, 0, 8, 1, 16, None, None, None, None) == 1   # only prior flags
