@@ -73,6 +73,9 @@ __device__ __forceinline__ float ssmax_c(bool ssmax, float s, int n) {
   return ssmax ? s * __logf((float)n) : 1.0f;
 }
 
+// max(a, b, c) (one v_max3_f32)
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
 // Lane exchange with lane ^ 32 (the other half of a wave64).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

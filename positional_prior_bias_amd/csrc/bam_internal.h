@@ -60,7 +60,7 @@ struct SkipArgs {
   int tab_stride;
   const float* s;         // SSMax strength (null without SSMax)
   bool ssmax;
-  float* smax;            // [H][T] suffix maximum of the bias over distances
+  float* smax;            // [H][ceil(T / 64)] suffix maximum of the bias at chunk starts
   float* rowu;            // [B*H][T]
   float* rowv;            // [B*H][T]
   float* kpart;           // [B*H][nparts] per-block max |k|

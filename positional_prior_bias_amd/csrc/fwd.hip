@@ -20,8 +20,9 @@
 //     (stored in reverse distance order, so a lane's values are read in register order),
 //     and the MFMA returns q.k + sqrt(Dh) b directly.  Distances the causal mask forbids
 //     hold -inf in that window, so masking is free as well.
-//   * The running max is rescaled lazily: O and l are rescaled only when a row max grows
-//     by more than 2^8.
+//   * The running max moves lazily: the reference max of a row changes only when a tile's
+//     max exceeds it by more than 2^8 (O and l are multiplied by the factor every tile, by
+//     1 when the reference holds; this keeps the tile one basic block).
 //   * O^T = V^T P^T with P and V in fp16 (v_mfma_f32_32x32x16_f16): P^T is fed from the
 //     S^T accumulators without any lane exchange (the contraction index runs over the keys
 //     in the order the accumulator holds them); V^T comes from transposing LDS reads of the
@@ -271,21 +272,23 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; x += 4) {
-          mxa = __builtin_fmaxf(mxa, __builtin_fmaxf(sacc[qb2][kb][x], sacc[qb2][kb][x + 1]));
-          mxb = __builtin_fmaxf(mxb, __builtin_fmaxf(sacc[qb2][kb][x + 2], sacc[qb2][kb][x + 3]));
+          mxa = max3(mxa, sacc[qb2][kb][x], sacc[qb2][kb][x + 1]);
+          mxb = max3(mxb, sacc[qb2][kb][x + 2], sacc[qb2][kb][x + 3]);
         }
       const float mx = max_xor32(__builtin_fmaxf(mxa, mxb));
       const float cand = Cl[qb2] * mx;
-      if (__any(cand > m[qb2] + kLazy)) {
-        const float m_new = fmaxf(m[qb2], cand);
-        const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(m[qb2] - m_new);
-        m[qb2] = m_new;
-        l[qb2] *= sc;
+      // The decision is wave-uniform and usually "keep"; only the scale factor depends on
+      // it and O is always multiplied (by 1 when the max holds).  A branch around the
+      // multiply made the compiler copy all of O on every tile to merge the two paths.
+      const bool up = __any(cand > m[qb2] + kLazy);
+      const float m_new = up ? fmaxf(m[qb2], cand) : m[qb2];
+      const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(m[qb2] - m_new);
+      m[qb2] = m_new;
+      l[qb2] *= sc;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int x = 0; x < 16; ++x) oacc[qb2][db][x] *= sc;
-      }
+        for (int x = 0; x < 16; ++x) oacc[qb2][db][x] *= sc;
       const float m_use = (m[qb2] == kNegInf) ? 0.f : m[qb2];
       // l sums the same fp16-rounded weights the PV product uses (v_dot2 with (1, 1)): O is
       // normalised by it, an exact convex combination of the rows of V under those weights,

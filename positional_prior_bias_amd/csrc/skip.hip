@@ -22,11 +22,14 @@
 // Three small kernels, all reading what the forward reads anyway (Q, K once; the table):
 //   skip_rows_kernel   per row: u_i = |q_i| / sqrt(Dh), v_i = R_i + u_i Kmax, and a per-block
 //                      max of |k_j|;
-//   skip_suffix_kernel per head: S(d) for d in [0, T - 1] from the forward's table;
-//   skip_plan_kernel   per query block: Kmax, R = min_i R_i, the largest distance D* with
-//                      S(D*) >= R (a 64-way search; S is non-increasing), and the first key
-//                      tile floor((i0 - D*) / 64).
-// For rows i >= i0 and keys j < i0 - D*, i - j > D*, so b(i - j) <= S(D* + 1) < R <= R_i.
+//   skip_suffix_kernel per head: C(c) = S(64 c), the suffix maximum at chunk starts, from
+//                      the forward's table;
+//   skip_plan_kernel   per query block: Kmax, R = min_i R_i, the largest chunk c* with
+//                      C(c*) >= R (a 64-way search; C is non-increasing), and the first key
+//                      tile floor((i0 - 64 c* - 63) / 64).
+// For rows i >= i0 and keys j < i0 - 64 c* - 63, i - j >= 64 (c* + 1), so
+// b(i - j) <= C(c* + 1) < R <= R_i.  (Chunk granularity can only keep more keys than the
+// exact largest distance would; the plan is in whole tiles anyway.)
 #include <float.h>
 
 #include "bam_device.h"
@@ -98,31 +101,38 @@ __global__ void __launch_bounds__(256) skip_rows_kernel(SkipArgs a, int T, int H
     a.kpart[(size_t)bh * gridDim.x + blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
-// S(d) = max_{d' in [d, T - 1]} b(d') for one head; b(d) is the forward table's entry
-// tab_d0 - d divided by sqrt(Dh).  Each thread owns a run of consecutive distances.
+// C(c) = S(64 c) = max_{d >= 64 c} b(d) for one head: the maxima of the 64-distance chunks
+// (one wave per chunk, coalesced), then their suffix maximum (each thread a run of chunks,
+// then a scan over the runs).  The forward's table holds sqrt(Dh) b at entry tab_d0 - d.
 __global__ void __launch_bounds__(1024) skip_suffix_kernel(SkipArgs a, int T, float rs) {
   const int h = blockIdx.x;
   const float* th = a.tab + (size_t)h * a.tab_stride + a.tab_d0;   // th[-d] = sqrt(Dh) b(d)
-  float* sh = a.smax + (size_t)h * T;
-  const int tid = threadIdx.x;
-  const int run = (T + 1023) / 1024;
-  const int d0 = min(T, tid * run), d1 = min(T, d0 + run);
+  const int nch = (T + 63) / 64;
+  float* ch = a.smax + (size_t)h * nch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int c = wave; c < nch; c += 16) {
+    const int d = 64 * c + lane;
+    const float mx = wave_max(d < T ? th[-d] : kNegInf);
+    if (lane == 0) ch[c] = mx * rs;
+  }
+  __syncthreads();
+  const int run = (nch + 1023) / 1024;
+  const int c0 = min(nch, tid * run), c1 = min(nch, c0 + run);
   float mx = kNegInf;
-  for (int d = d0; d < d1; ++d) mx = fmaxf(mx, th[-d]);
+  for (int c = c0; c < c1; ++c) mx = fmaxf(mx, ch[c]);
   __shared__ float suf[1024];
   suf[tid] = mx;
   __syncthreads();
-  // inclusive suffix maximum over the 1024 runs
-  for (int o = 1; o < 1024; o <<= 1) {
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive suffix maximum over the runs
     const float x = tid + o < 1024 ? fmaxf(suf[tid], suf[tid + o]) : suf[tid];
     __syncthreads();
     suf[tid] = x;
     __syncthreads();
   }
   float acc = tid + 1 < 1024 ? suf[tid + 1] : kNegInf;
-  for (int d = d1 - 1; d >= d0; --d) {
-    acc = fmaxf(acc, th[-d]);
-    sh[d] = acc * rs;
+  for (int c = c1 - 1; c >= c0; --c) {
+    acc = fmaxf(acc, ch[c]);
+    ch[c] = acc;
   }
 }
 
@@ -146,22 +156,25 @@ __global__ void __launch_bounds__(64) skip_plan_kernel(SkipArgs a, int T, int H,
   }
   r = wave_min(r);
   int tile = 0;
-  const float* sh = a.smax + (size_t)h * T;
-  if (r > kNegInf && i0 > 0 && !(sh[i0] >= r)) {
-    // invariant: S(lo) >= r or lo = 0; S(hi) < r.  S is non-increasing, so the probes that
-    // pass form a prefix of the lanes.
-    int lo = 0, hi = i0;
+  const int nch = (T + 63) / 64;
+  const float* cs = a.smax + (size_t)h * nch;   // C(c) = S(64 c), non-increasing in c
+  const int cmax = i0 / 64;
+  if (r > kNegInf && i0 > 0 && !(cs[cmax] >= r)) {
+    // c* = the largest chunk with C(c*) >= r (0 if none).  Invariant: C(lo) >= r or lo = 0;
+    // C(hi) < r.  The probes that pass form a prefix of the lanes.
+    int lo = 0, hi = cmax;
     while (hi - lo > 1) {
       const int step = (hi - lo + 63) / 64;
       const int p = lo + step * (lane + 1);
-      const bool ok = p < hi && sh[p] >= r;
+      const bool ok = p < hi && cs[p] >= r;
       const unsigned long long bal = __ballot(ok);
       const int last = bal ? 63 - __builtin_clzll(bal) : -1;   // last passing probe
       const int nlo = last >= 0 ? lo + step * (last + 1) : lo;
       hi = min(hi, lo + step * (last + 2));
       lo = nlo;
     }
-    tile = (i0 - lo) / 64;
+    // every d >= 64 (c* + 1) has b(d) <= C(c* + 1) < r: keys j < i0 - 64 c* - 63 are out
+    tile = max(0, i0 - 64 * lo - 63) / 64;
   }
   if (lane == 0) a.first_tile[bid] = tile;
 }
