@@ -86,21 +86,6 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Scheduling hint for the basic block it closes: `lead` VALU ops, then NMFMA times one MFMA
-// followed by `per` VALU ops (masks: 0x2 VALU, 0x8 MFMA).
-#define BAM_INTERLEAVE(NMFMA, lead, per)                            \
-  do {                                                              \
-    __builtin_amdgcn_sched_group_barrier(0x002, (lead), 0);         \
-    _Pragma("unroll") for (int bam_i_ = 0; bam_i_ < (NMFMA); ++bam_i_) { \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            \
-      __builtin_amdgcn_sched_group_barrier(0x002, (per), 0);        \
-    }                                                               \
-  } while (0)
-
-}  // namespace bam
-
-namespace bam {
-
 // XOR swizzle (Gray code of the row) of the 16-byte chunks of a row-major bf16 tile in
 // LDS, so 16-byte reads of one chunk column across consecutive rows spread over banks.
 __device__ __forceinline__ int swz_chunk(int r, int mask) { return (r ^ (r >> 1)) & mask; }
@@ -227,17 +212,6 @@ __device__ __forceinline__ int vswz(int r) {
     __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (0 << 8)); \
     __builtin_amdgcn_s_barrier();                                                     \
     asm volatile("" ::: "memory");                                                    \
-  } while (0)
-
-// Scheduling hint for the basic block it closes: `lead` VALU ops, then NMFMA times one MFMA
-// followed by `per` VALU ops (masks: 0x2 VALU, 0x8 MFMA).
-#define BAM_INTERLEAVE(NMFMA, lead, per)                            \
-  do {                                                              \
-    __builtin_amdgcn_sched_group_barrier(0x002, (lead), 0);         \
-    _Pragma("unroll") for (int bam_i_ = 0; bam_i_ < (NMFMA); ++bam_i_) { \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            \
-      __builtin_amdgcn_sched_group_barrier(0x002, (per), 0);        \
-    }                                                               \
   } while (0)
 
 }  // namespace bam
