@@ -102,15 +102,10 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   float Cl[NQB], m[NQB], l[NQB];
   const float sqrtD = __builtin_sqrtf((float)DH);
   const float sh = a.ssmax ? a.s[h] : 1.0f;
+  u32x4 qw[NQB][KS];
 #pragma unroll
   for (int qb2 = 0; qb2 < NQB; ++qb2) {
     const int i = iw + 32 * qb2 + ql;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (i < T) w = *(const u32x4*)(Q + (size_t)i * DH + 16 * ks + 8 * hh);
-      qf[qb2][ks] = as_bf16x8(w);
-    }
     const float c = ssmax_c(a.ssmax, sh, CAUSAL ? i + 1 : T);
     // logit in log2 units = Cl * (q.k + sqrt(Dh) b); c = 0 only when one key is visible
     Cl[qb2] = fmaxf(c * kLog2e / sqrtD, FLT_MIN);
@@ -347,14 +342,36 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
   // ---- three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load.  Q is
   // in registers before the first tile load is issued (the compiler would otherwise wait
   // for it, and so for every load in flight, inside the loop).
+  // Q is loaded between the first two tiles with buffer loads the compiler does not track
+  // (rows at or beyond T load as zeros), so one wait covers tile 0 and Q and tile 1 stays
+  // in flight; the empty asm statements after the wait make Q's registers defined there.
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, jb);
+  {
+    const i32x4 rQ = buffer_rsrc(Q, (uint32_t)T * DH * 2);
+#pragma unroll
+    for (int qb2 = 0; qb2 < NQB; ++qb2) {
+      const int i = iw + 32 * qb2 + ql;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = (uint32_t)(i * DH + 16 * ks + 8 * hh) * 2u;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(qw[qb2][ks]) : "v"(off), "s"(rQ) : "memory");
+      }
+    }
+  }
   if (ntiles > 1) {
     issue_tile(tB, jb + kNK);
-    BAM_WAIT_VMCNT(LPT);       // this wave's loads of tile 0 landed (tile 1 may be in flight)
+    BAM_WAIT_VMCNT(LPT);       // tile 0 and Q landed (tile 1 may be in flight)
   } else {
     BAM_WAIT_VMCNT(0);
   }
+#pragma unroll
+  for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      asm volatile("" : "+v"(qw[qb2][ks]));
+      qf[qb2][ks] = as_bf16x8(qw[qb2][ks]);
+    }
   convert_v(tA);
   BAM_BARRIER_VMCNT(63);       // publish tile 0
   // every wave has waited for its loads of tile t + 1 (in compute_tile); publish it
