@@ -120,7 +120,8 @@ int bam_version(void);
  * bam_prior_table - the per-head distance table of the GGD prior.
  *
  * Writes tab[h * n + t] = b_h(d0 + t) for t in [0, n), h in [0, H), in float32, where
- * b_h is the bias above (computed in float64, rounded once).  With dalpha / dbeta
+ * b_h is the bias above (the exponent in float64, the result within about 2 float32 ulps,
+ * rounded once to float32).  With dalpha / dbeta
  * non-NULL it also writes the parameter derivatives of the bias,
  *   dalpha[h * n + t] = db/dalpha = beta u^beta / alpha,
  *   dbeta [h * n + t] = db/dbeta  = -u^beta ln u          (both 0 where u = 0).

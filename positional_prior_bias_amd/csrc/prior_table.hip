@@ -5,8 +5,8 @@
 // d = i - j (query minus key).  The bias depends on the distance only, so one row of
 // n values per head replaces the dense T x T matrix; it is rebuilt on every call since
 // alpha and beta are trained parameters ("Bayesian Attention Mechanism",
-// "Implementation Details").  One pow per (head, distance), evaluated in float64 and
-// rounded once to float32.
+// "Implementation Details").  One power per (head, distance): the exponent in float64,
+// the final 2^fraction in float32 (pow_pos), rounded once to float32.
 //
 // The same table carries any other bias that depends on the head and i - j only.  The
 // Sandwich bias (attention-gym "Score Mods", "Sandwich") is the inner product of two
@@ -28,6 +28,20 @@ namespace bam {
 // trunc(d_bar) / 2, at most kSandwichMaxFreq; beyond that the entries are NaN), and the
 // derivative tables are zero.
 constexpr int kSandwichMaxFreq = 512;
+
+// u^e for u > 0: the exponent y = e log2(u) in float64, split into an integer n and a
+// fraction f in [0, 1); 2^f in float32 (one v_exp_f32, about 1 ulp), scaled by 2^n
+// exactly.  The result is within about 2 float32 ulps of the float64 pow, which it
+// replaces because the table is rounded to float32 anyway and pow costs several times as
+// much.  log2(u) is returned for the derivative tables.  Exponents beyond +-1000 (the
+// value is then 0 or inf in float32) go through pow.
+__device__ __forceinline__ double pow_pos(double u, double e, double& l2) {
+  l2 = log2(u);
+  const double y = e * l2;
+  if (!(fabs(y) < 1000.0)) return pow(u, e);
+  const double n = floor(y);
+  return ldexp((double)exp2f((float)(y - n)), (int)n);
+}
 
 __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restrict__ alpha,
                                                           const float* __restrict__ beta,
@@ -77,9 +91,10 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
     const double em = exp(m), emi = exp(-m);
     const double x = -(double)d - (em - emi);
     const double g = fabs(x) + (double)BAM_REF_EPS;
-    b = -exp(a) * pow(g, be);
+    double l2g;
+    b = -exp(a) * pow_pos(g, be, l2g);
     da = b;
-    db = b * log(g);
+    db = b * l2g * 0.6931471805599453;   // b ln g
     const double sg = x > 0.0 ? 1.0 : (x < 0.0 ? -1.0 : 0.0);
     dm = -b * be * sg / g * (em + emi);
   } else {
@@ -91,10 +106,11 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
     } else if (u == 0.0) {
       b = be > 0.0 ? 0.0 : -__builtin_huge_val();  // beta < 0 at u = 0: precondition violated
     } else {
-      const double p = pow(u, be);
+      double l2u;
+      const double p = pow_pos(u, be, l2u);
       b = -p;
       da = be * p / a;
-      db = -p * log(u);
+      db = -p * l2u * 0.6931471805599453;  // -p ln u
       dm = be * p / x;                             // db/dmu, dx/dmu = -1
     }
   }
