@@ -75,6 +75,24 @@ class Timer:
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return e0.elapsed_time(e1) / steps, wall
 
+    def cold_launch(self, fn, reps):
+        """Median duration of one launch right after a 1 GiB device write, which evicts the
+        inputs from L2 and the 256 MB MALL (each launch timed alone with an event pair)."""
+        torch = self.torch
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(reps):
+            junk.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        del junk
+        return sorted(times)[len(times) // 2]
+
     def per_launch(self, fn, launches, warmup=2):
         """Average duration of one launch of `fn`'s kernel: one event pair around `launches`
         back-to-back launches on the stream the kernel runs on."""
@@ -103,7 +121,7 @@ def device_inputs(torch, w, with_grad=False):
     return out
 
 
-def bench_fwd(torch, bam, w, steps, warmup, timer, name):
+def bench_fwd(torch, bam, w, steps, warmup, timer, name, cold=False):
     x = device_inputs(torch, w)
     B, H, T, Dh = w.q.shape
     o = torch.empty((B, H, T, Dh), dtype=torch.bfloat16, device="cuda")
@@ -115,10 +133,13 @@ def bench_fwd(torch, bam, w, steps, warmup, timer, name):
                          o=o, lse=lse, workspace=ws, table_ready=table_ready)
     ms, wall = timer.steps(call, steps, warmup)
     kern_ms = timer.per_launch(lambda: call(True), max(steps, 10))
+    cold_ms = timer.cold_launch(lambda: call(True), 10) if cold else None
     flops = fwd_flops(B, H, T, Dh)
     algo_bytes = 4 * B * H * T * Dh * 2 + B * H * T * 4   # Q, K, V read + O write (bf16) + lse
     log(f"[{name}] step {ms:.4f} ms (wall {wall:.4f}), fwd kernel {kern_ms:.4f} ms")
-    return dict(ms=ms, wall_ms=wall, kernel_ms=kern_ms, flops=flops, bytes=algo_bytes,
+    if cold_ms is not None:
+        log(f"[{name}] cold fwd kernel (caches flushed by a 1 GiB write) {cold_ms:.4f} ms")
+    return dict(ms=ms, wall_ms=wall, kernel_ms=kern_ms, cold_kernel_ms=cold_ms, flops=flops, bytes=algo_bytes,
                 tflops=flops / ms / 1e9, kernel_tflops=flops / kern_ms / 1e9,
                 kernel_gbs=algo_bytes / kern_ms / 1e6)
 
@@ -321,13 +342,15 @@ def main():
 
     log("[fwd512] generating inputs")
     w2 = wl.training_shape()
-    r512 = bench_fwd(torch, bam, w2, args.steps, args.warmup, timer, "fwd512")
+    r512 = bench_fwd(torch, bam, w2, args.steps, args.warmup, timer, "fwd512", cold=True)
     out_parts = {"fwd_T512": {
         "workload": "causal fwd B=32 H=12 T=512 Dh=64 bf16, SSMax on",
         "ms": round(r512["ms"], 5), "TFLOP/s": round(r512["tflops"], 2),
         "pct_mfma_peak": round(100 * r512["tflops"] / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": round(r512["kernel_ms"], 5), "kernel_TFLOP/s": round(r512["kernel_tflops"], 2),
         "kernel_algorithmic_GB/s": round(r512["kernel_gbs"], 1),
+        "cold_kernel_ms": round(r512["cold_kernel_ms"], 5),
+        "cold_kernel_TFLOP/s": round(r512["flops"] / r512["cold_kernel_ms"] / 1e9, 2),
         "pct_hbm_peak": round(100 * r512["kernel_gbs"] / PEAK_HBM_GBS, 2)}}
 
     if "fwd32k" in parts:
