@@ -73,7 +73,9 @@ __device__ __forceinline__ float ssmax_c(bool ssmax, float s, int n) {
   return ssmax ? s * __logf((float)n) : 1.0f;
 }
 
-// max(a, b, c) (one v_max3_f32)
+// max(a, b, c).  Written in C on purpose: an inline-asm v_max3_f32 is opaque to the
+// compiler's hazard checks, which then do not wait for a preceding MFMA to finish writing
+// the registers it reads.
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // Lane exchange with lane ^ 32 (the other half of a wave64).

@@ -84,7 +84,7 @@ CASES = [
     (300, 64, False, True, (0.2, 1.2), 0.0),
     (513, 32, True, True, (0.2, 1.2), 0.0),
     (700, 128, False, False, (0.5, 2.0), 0.0),
-    # long sequences (the 512-row ping-pong kernel serves Dh = 64 from T = 2048 on)
+    # long sequences (many key tiles per work-group, a ragged last tile)
     (2048, 64, True, True, (0.1, 0.9), 0.0),
     (2100, 64, True, True, (-0.8, -0.1), -0.5),
     (2333, 64, False, True, (0.2, 1.2), 0.0),
