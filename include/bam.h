@@ -154,8 +154,9 @@ bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float
  * Without BAM_CAUSAL every query sees all T keys (n_i = T).
  * o: [B, H, T, Dh] of o_dtype (BAM_BF16 output is the round-to-nearest-even of the
  * float32 result).  lse: [B, H, T] float32, natural log.
- * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128} (bf16 MFMA, fp32 accumulate);
- * in_dtype BAM_F32 with Dh in {32, 64} (fp32 throughout).  BAM_SKIP_FAR: see above.
+ * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128} (bf16 MFMA, fp32 accumulate) and
+ * T * Dh * 2 < 2^31 bytes per (b, h); in_dtype BAM_F32 with Dh in {32, 64} (fp32
+ * throughout).  Larger requests return BAM_EUNSUPPORTED.  BAM_SKIP_FAR: see above.
  */
 size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
 bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtype,

@@ -156,6 +156,8 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
     return BAM_EUNSUPPORTED;
   }
   if ((size_t)B * H * (size_t)T * Dh > ((size_t)1 << 40)) return BAM_EUNSUPPORTED;
+  // the bf16 kernel addresses one (b, h) slab of Q, K, V with 32-bit buffer offsets
+  if (in_dtype == BAM_BF16 && (size_t)T * Dh * 2 > (size_t)0x7fffffff) return BAM_EUNSUPPORTED;
   if (workspace_bytes < bam_fwd_workspace_size(B, H, T, Dh, flags)) return BAM_EWORKSPACE;
 
   const bool causal = (flags & BAM_CAUSAL) != 0;

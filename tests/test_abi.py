@@ -85,6 +85,7 @@ def test_fwd_rejects_bad_arguments_before_launch(L):
     assert _fwd(L, q=8) == 1                      # misaligned
     assert _fwd(L, T=0) == 1
     assert _fwd(L, flags=64) == 1                 # unknown flag bit
+    assert _fwd(L, T=1 << 24, Dh=64) == 2         # one (b, h) slab beyond 32-bit offsets
     assert _fwd(L, flags=2 | 32) == 2             # skipping needs the causal bf16 path
     assert _fwd(L, flags=3 | 8 | 16) == 1         # two prior kinds at once
     assert _fwd(L, s=None) == 1                   # SSMax without s
