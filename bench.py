@@ -269,8 +269,21 @@ def bench_sweep(torch, bam, wl, timer):
     return out
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, seconds):
-    """fp64 oracle on whole (b, h) heads of the same batch until `seconds` have elapsed."""
+    """fp64 oracle on whole (b, h) heads of the same batch, in batch order, repeating the
+    batch until `seconds` have elapsed (so a batch that finishes early is timed over several
+    passes rather than one short one)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -280,20 +293,23 @@ def cpu_baseline(w, seconds):
     B, H, T, Dh = w.q.shape
     done = 0
     t0 = time.perf_counter()
-    for b in range(B):
-        for h in range(H):
-            oracle.attn_fwd(w.q[b:b + 1, h:h + 1], w.k[b:b + 1, h:h + 1], w.v[b:b + 1, h:h + 1], w.alpha[h:h + 1],
-                            w.beta[h:h + 1], w.mu[h:h + 1], w.s[h:h + 1], causal=True, ssmax=True)
-            done += 1
+    while time.perf_counter() - t0 < seconds:
+        for b in range(B):
+            for h in range(H):
+                oracle.attn_fwd(w.q[b:b + 1, h:h + 1], w.k[b:b + 1, h:h + 1], w.v[b:b + 1, h:h + 1],
+                                w.alpha[h:h + 1], w.beta[h:h + 1], w.mu[h:h + 1], w.s[h:h + 1], causal=True,
+                                ssmax=True)
+                done += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
             if time.perf_counter() - t0 >= seconds:
                 break
-        if time.perf_counter() - t0 >= seconds:
-            break
     el = time.perf_counter() - t0
     flops = fwd_flops(1, done, T, Dh)
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {B * H} (b,h) heads of the B={B},H={H},T={T},Dh={Dh} batch, every row, "
-                      f"{el:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise work single-threaded)"}
+            "sample": f"{done} (b,h) heads ({done / (B * H):.2f} passes over the B={B},H={H},T={T},Dh={Dh} batch), "
+                      f"every row, {el:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise work "
+                      f"single-threaded) on {_cpu_model()}"}
 
 
 def traffic_from_counters():
