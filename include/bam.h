@@ -93,8 +93,8 @@ typedef int bam_status;
  * scaled down per head,
  *   b_h(d) = sum_{i = 0}^{d_bar/2 - 1} cos(d / 10000^(2 i / d_bar)) / ratio_h,
  * with alpha[h] = ratio_h (the page uses 8 (h + 1) / H) and beta[h] = d_bar (the page uses
- * 128); mu is ignored.  The frequency count is trunc(beta[h]) / 2; above 512 frequencies
- * the bias is NaN.  The bias has no parameters: the backward's dalpha, dbeta and dmu are
+ * 128); mu is ignored.  The frequency count is trunc(beta[h]) / 2 (none below 2: a zero
+ * bias); above 512 frequencies, or for a NaN beta[h], the bias is NaN.  The bias has no parameters: the backward's dalpha, dbeta and dmu are
  * zero.  Not combinable with BAM_PRIOR_REF (BAM_EINVAL).  Accepted by every entry point. */
 #define BAM_PRIOR_SANDWICH 16u
 /* Prior-aware key skipping (bam_attn_fwd, causal bf16 only; BAM_EUNSUPPORTED otherwise).

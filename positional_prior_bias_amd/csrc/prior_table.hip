@@ -58,7 +58,10 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   __shared__ double inv_w[kSandwichMaxFreq];
   int nf = 0;
   if (kind == kPriorSandwich) {
-    nf = (int)beta[h] / 2;
+    // trunc(d_bar) / 2 frequencies; NaN or huge d_bar counts as too many (NaN entries)
+    const float db = beta[h];
+    const bool nan = (__float_as_uint(db) & 0x7fffffffu) > 0x7f800000u;   // by bits: built with -fno-honor-nans
+    nf = (nan || db >= 4096.0f) ? kSandwichMaxFreq + 1 : (db < 2.0f ? 0 : (int)db / 2);
     for (int i = threadIdx.x; i < kSandwichMaxFreq && i < nf; i += blockDim.x)
       inv_w[i] = pow(10000.0, 2.0 * i / (double)beta[h]);
     __syncthreads();

@@ -46,12 +46,18 @@ def test_prior_table_sandwich(d_bar):
         assert not np.any(host(g))
 
 
-def test_prior_table_sandwich_too_many_frequencies():
-    """Above 512 frequencies (d_bar >= 1026) the documented result is NaN."""
-    ratio = np.array([1.0, 1.0], np.float32)
-    dbar = np.array([1024.0, 1026.0], np.float32)
+def test_prior_table_sandwich_frequency_count_edges():
+    """Above 512 frequencies (d_bar >= 1026, also huge or NaN d_bar) the documented result
+    is NaN; d_bar below 2 keeps no frequency (zero bias, as the oracle's empty sum)."""
+    ratio = np.ones(6, np.float32)
+    dbar = np.array([1024.0, 1026.0, 3e9, np.nan, 1.5, -4.0], np.float32)
     tab = host(_bam().bam_prior_table_ex(dev(ratio), dev(dbar), None, -3, 7, prior="sandwich")[0])
-    assert np.all(np.isfinite(tab[0])) and np.all(np.isnan(tab[1]))
+    assert np.all(np.isfinite(tab[0]))
+    assert np.all(np.isnan(tab[1:4]))
+    assert not np.any(tab[4:])
+    d = np.arange(-3, 4)
+    for h in (4, 5):
+        assert np.array_equal(oracle.prior_bias_sandwich(d, 1.0, float(dbar[h])), np.zeros(7))
 
 
 def test_sandwich_with_prior_ref_rejected():
