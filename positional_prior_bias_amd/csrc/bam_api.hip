@@ -227,7 +227,7 @@ struct DecodeLayout {
 DecodeLayout decode_layout(int B, int H, int Lmax, int Dh) {
   DecodeLayout d;
   d.tab_stride = pad64(Lmax);
-  d.chunk = bam::decode_chunk_keys(Lmax, Dh);
+  d.chunk = bam::decode_chunk_keys(Lmax, Dh, B * H);
   d.nsplit = (Lmax + d.chunk - 1) / d.chunk;
   d.tab_off = 0;
   d.part_off = align_up((size_t)H * d.tab_stride * sizeof(float));

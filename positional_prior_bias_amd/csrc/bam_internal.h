@@ -91,7 +91,7 @@ struct DecodeArgs {
   float* lse;
 };
 
-int decode_chunk_keys(int Lmax, int Dh);
+int decode_chunk_keys(int Lmax, int Dh, int BH);
 hipError_t launch_decode(const DecodeArgs& a, int Dh, hipStream_t stream);
 
 struct BwdArgs {
