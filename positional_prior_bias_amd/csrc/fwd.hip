@@ -60,7 +60,7 @@ struct FwdTile {
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
 template <int DH, bool CAUSAL, int NQB>
-__global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a, int nqb) {
+__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   constexpr int QW = 32 * NQB;          // query rows per wave
   constexpr int MQ = 4 * QW;            // query rows per work-group
   constexpr int TW = MQ + kNK;          // distance-window entries per tile (multiple of 64)
@@ -203,8 +203,11 @@ __global__ void __launch_bounds__(256, CAUSAL ? 2 : 1) fwd_bf16_kernel(FwdArgs a
 
   auto compute_tile = [&](const FwdTile<DH, TW>& tl, FwdTile<DH, TW>& nx, int t) {
     const int j0 = jb + t * kNK;
-    // a wave whose rows all precede this tile's keys has nothing to do (causal)
-    if (CAUSAL && j0 > iw + QW - 1) {
+    // A wave whose rows all precede this tile's keys has nothing to do (causal).  Without
+    // the mask the second test never holds (tiles end before T), but the branch splits the
+    // tile into its own scheduling region: as one region with the loop around it, the
+    // compiler's schedule needs more than the 256 registers of two waves per SIMD.
+    if ((CAUSAL && j0 > iw + QW - 1) || (!CAUSAL && j0 >= T)) {
       convert_next(nx, t);
       return;
     }
