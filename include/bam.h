@@ -169,8 +169,8 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
  * bam_fwd_skip_plan_offset - where a BAM_SKIP_FAR forward leaves its skipping plan.
  *
  * After bam_attn_fwd with these flags (which must include BAM_CAUSAL | BAM_SKIP_FAR), the
- * workspace holds, at byte *offset, *count = ceil(T / R) * B * H int32 values, R = 256
- * query rows per block for Dh <= 64 and 128 for Dh = 128.  Entry qb * B * H + b * H + h
+ * workspace holds, at byte *offset, *count = ceil(T / R) * B * H int32 values, R = 128
+ * query rows per block for Dh = 128 and for Dh = 64 with T <= 1024, else R = 256.  Entry qb * B * H + b * H + h
  * is the number of leading 64-key tiles that query block qb of (b, h) left out.  For
  * measuring how much work the prior saved; the plan is rewritten by every such call.
  * Returns BAM_EUNSUPPORTED for flags without BAM_CAUSAL | BAM_SKIP_FAR or an unsupported Dh.

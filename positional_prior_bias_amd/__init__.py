@@ -15,7 +15,7 @@ import os
 __all__ = [
     "BAM_BF16", "BAM_F32", "BAM_CAUSAL", "BAM_SSMAX", "BAM_TABLE_READY", "BAM_PRIOR_REF", "BAM_REF_EPS",
     "BAM_PRIOR_SANDWICH", "sandwich_ratios", "alibi_slopes", "BAM_SKIP_FAR", "bam_fwd_skip_plan_offset",
-    "fwd_skipped_fraction",
+    "fwd_skipped_fraction", "fwd_rows_per_block",
     "BamError", "lib", "lib_path",
     "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_attn_bwd",
@@ -248,13 +248,19 @@ def bam_fwd_skip_plan_offset(B, H, T, Dh, flags):
     return int(off.value), int(cnt.value)
 
 
+def fwd_rows_per_block(Dh, T):
+    """Query rows per work-group of the bf16 forward (the rule include/bam.h states for the
+    skipping plan): 128 for Dh = 128 and for Dh = 64 with T <= 1024, else 256."""
+    return 128 if (Dh == 128 or (Dh == 64 and T <= 1024)) else 256
+
+
 def fwd_skipped_fraction(workspace, B, H, T, Dh, flags):
     """Fraction of the causal forward's (query block, key tile) pairs that the last
     BAM_SKIP_FAR call on `workspace` left out (reads the plan back to the host)."""
     torch = _torch()
     off, cnt = bam_fwd_skip_plan_offset(B, H, T, Dh, flags)
     plan = workspace[off:off + 4 * cnt].view(torch.int32).cpu().long()
-    rows = 256 if Dh <= 64 else 128
+    rows = fwd_rows_per_block(Dh, T)
     nqb = cnt // (B * H)
     qb = torch.arange(nqb).repeat_interleave(B * H)
     total = ((torch.clamp((qb + 1) * rows, max=T) + 63) // 64).sum().item()

@@ -76,7 +76,7 @@ FwdLayout fwd_layout(int B, int H, int T, int Dh, unsigned flags) {
   L.total = align_up((size_t)H * g.stride * sizeof(float));
   if ((flags & BAM_SKIP_FAR) && causal && Dh > 0 && Dh % 8 == 0 && Dh <= 128) {
     const size_t BH = (size_t)B * H;
-    L.nqb = (T + bam::fwd_bf16_rows_per_block(Dh) - 1) / bam::fwd_bf16_rows_per_block(Dh);
+    L.nqb = (T + bam::fwd_bf16_rows_per_block(Dh, T) - 1) / bam::fwd_bf16_rows_per_block(Dh, T);
     L.nparts = (T + bam::skip_rows_per_block(Dh) - 1) / bam::skip_rows_per_block(Dh);
     L.smax_off = L.total;
     L.rowu_off = L.smax_off + align_up((size_t)H * T * sizeof(float));
@@ -209,7 +209,7 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
     sk.rowv = (float*)(ws + L.rowv_off);
     sk.kpart = (float*)(ws + L.kpart_off);
     sk.first_tile = (int32_t*)(ws + L.first_off);
-    e = bam::launch_fwd_skip_plan(sk, B, H, T, Dh, bam::fwd_bf16_rows_per_block(Dh), st);
+    e = bam::launch_fwd_skip_plan(sk, B, H, T, Dh, bam::fwd_bf16_rows_per_block(Dh, T), st);
     if (e != hipSuccess) return BAM_EHIP;
     a.first_tile = sk.first_tile;
   }

@@ -46,8 +46,14 @@ struct FwdArgs {
   const int32_t* first_tile;   // per work-group first key tile (prior-aware skipping), or null
 };
 
-// Query rows per work-group of the bf16 forward kernel.
-constexpr int fwd_bf16_rows_per_block(int Dh) { return Dh <= 64 ? 256 : 128; }
+// Query rows per work-group of the bf16 forward kernel: two 32-row blocks per wave (256
+// rows) for Dh <= 64, one (128 rows) for Dh = 128 and for Dh = 64 up to kFwdShortT.
+// Short sequences have few key tiles per work-group, so finer work-groups balance the
+// causal triangle better than the operand reuse of two blocks per wave pays.
+constexpr int kFwdShortT = 1024;
+constexpr int fwd_bf16_rows_per_block(int Dh, int T) {
+  return (Dh == 128 || (Dh == 64 && T <= kFwdShortT)) ? 128 : 256;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int Dh, hipStream_t stream);
 

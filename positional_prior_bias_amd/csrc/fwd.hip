@@ -7,8 +7,10 @@
 // the exact result of the dense definition up to float rounding.
 //
 // bf16 kernel design (wave64):
-//   * A work-group of 4 waves owns 256 query rows of one (b, h) (128 for Dh = 128); each
-//     wave owns 64 rows as two 32-row blocks that share every K and V^T operand read.
+//   * A work-group of 4 waves owns 256 query rows of one (b, h); each wave owns 64 rows as
+//     two 32-row blocks that share every K and V^T operand read.  For Dh = 128, and for
+//     Dh = 64 with short sequences (finer work-groups balance the causal triangle), a wave
+//     owns one 32-row block and a work-group 128 rows.
 //   * Key tiles of 64 go straight from HBM to LDS (buffer loads to LDS, issued from inline
 //     assembly so the compiler does not make every LDS read wait for them), three tiles in
 //     flight, one barrier per tile; rows at or beyond T load as zeros.
@@ -533,15 +535,25 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a, int nqb) {
   }
 }
 
-template <int DH, bool CAUSAL>
-hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NQB = DH <= 64 ? 2 : 1;
+template <int DH, bool CAUSAL, int NQB>
+hipError_t launch_bf16_nqb(const FwdArgs& a, hipStream_t stream) {
   constexpr int MQ = 4 * 32 * NQB;
-  static_assert(MQ == fwd_bf16_rows_per_block(DH), "rows per work-group");
   const int nqb = (a.T + MQ - 1) / MQ;
   const long nblocks = (long)nqb * a.B * a.H;
   hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL, NQB>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, nqb);
   return hipGetLastError();
+}
+
+template <int DH, bool CAUSAL>
+hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (DH == 128) {
+    return launch_bf16_nqb<DH, CAUSAL, 1>(a, stream);
+  } else if constexpr (DH == 64) {
+    if (fwd_bf16_rows_per_block(DH, a.T) == 128) return launch_bf16_nqb<DH, CAUSAL, 1>(a, stream);
+    return launch_bf16_nqb<DH, CAUSAL, 2>(a, stream);
+  } else {
+    return launch_bf16_nqb<DH, CAUSAL, 2>(a, stream);
+  }
 }
 
 template <int DH, bool CAUSAL>

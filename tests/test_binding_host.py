@@ -38,14 +38,14 @@ def test_parameter_helpers():
     assert np.allclose(bam.sandwich_ratios(12).numpy(), 8 * np.arange(1, 13) / 12, rtol=1e-7)
 
 
-@pytest.mark.parametrize("T,Dh", [(512, 64), (2100, 64), (700, 128), (300, 32)])
+@pytest.mark.parametrize("T,Dh", [(512, 64), (1024, 64), (1025, 64), (2100, 64), (700, 128), (300, 32)])
 def test_skipped_fraction_arithmetic(T, Dh):
     """fwd_skipped_fraction reads the plan at the offset the library reports and divides by
     the causal tile count of each query block."""
     B, H = 2, 3
     flags = bam.BAM_CAUSAL | bam.BAM_SKIP_FAR
     off, cnt = bam.bam_fwd_skip_plan_offset(B, H, T, Dh, flags)
-    rows = 256 if Dh <= 64 else 128
+    rows = 128 if (Dh == 128 or (Dh == 64 and T <= 1024)) else 256   # include/bam.h
     nqb = (T + rows - 1) // rows
     assert cnt == nqb * B * H
     assert bam.bam_fwd_workspace_size(B, H, T, Dh, flags) >= off + 4 * cnt

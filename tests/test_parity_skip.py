@@ -65,7 +65,8 @@ def _case(w, ssmax=True, prior=None):
     return o2, l2, frac
 
 
-@pytest.mark.parametrize("T,Dh,ssmax", [(2100, 64, True), (1500, 32, True), (1100, 128, True), (2100, 64, False)])
+@pytest.mark.parametrize("T,Dh,ssmax", [(2100, 64, True), (1000, 64, True), (1500, 32, True), (1100, 128, True),
+                                        (2100, 64, False)])
 def test_skip_local_heads(T, Dh, ssmax):
     """Local heads (beta = 1 and 0.8, alpha = 1 .. 8) skip most tiles; results unchanged."""
     H = 4
