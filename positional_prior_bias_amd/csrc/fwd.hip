@@ -51,18 +51,18 @@ constexpr int kNK = 64;    // keys per tile
 // TW + 16 floats apart: copy c then starts at 16-byte bank group 4 c, and the 16 lanes of
 // one LDS cycle (4 consecutive groups of 4 lanes, each lane group spanning the 4 copies)
 // hit 16 distinct bank groups.
-template <int DH, int TW>
+template <int DH, int TW, int NCOPY>
 struct FwdTile {
   uint16_t k[kNK * DH];
   uint16_t v[kNK * DH];
-  float w[4][TW + 16];
+  float w[NCOPY][TW + 16];
 };
 
 
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
 template <int DH, bool CAUSAL, int NQB>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
+__global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   constexpr int QW = 32 * NQB;          // query rows per wave
   constexpr int MQ = 4 * QW;            // query rows per work-group
   constexpr int TW = MQ + kNK;          // distance-window entries per tile (multiple of 64)
@@ -70,14 +70,20 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   constexpr int KS = DH / 16;           // MFMA k-steps over the head dimension
   constexpr int DB = DH / 32;           // 32-row blocks of O^T
   constexpr int CPW = kNK * KCH / 256;  // 1 KiB direct loads per wave per tensor
-  constexpr int WPW = TW / 64;          // window loads per wave (4 copies x TW/64 over 4 waves)
+  // Copies of the window: 4 (each lane's runs of 4 distances are one 16-byte read); 2 for
+  // Dh = 64 with one query block per wave (8-byte reads), which keeps the work-group's LDS
+  // under a third of the CU's so three work-groups (three waves per SIMD) fit.
+  constexpr int NCOPY = (DH == 64 && NQB == 1) ? 2 : 4;
+  constexpr int NWL = NCOPY * (TW / 64);          // window loads per tile (all waves)
+  constexpr int WPW = (NWL + 3) / 4;              // window loads per wave; surplus slots repeat one
+  static_assert(NCOPY == 4 || NWL <= 4 * WPW, "window loads");
   constexpr int LPT = 2 * CPW + WPW;    // direct-load instructions per wave per tile
   constexpr float kLazy = 8.0f;         // rescale only when a row max grows by > 2^8
   static_assert(kNK * KCH % 256 == 0, "tile must split into 1 KiB wave loads");
   static_assert(LPT < 64, "vmcnt range");
 
   // three buffers as distinct objects: the tile being read, and up to two being filled
-  __shared__ __attribute__((aligned(16))) FwdTile<DH, TW> tA, tB, tC;
+  __shared__ __attribute__((aligned(16))) FwdTile<DH, TW, NCOPY> tA, tB, tC;
 
   const int BH = a.B * a.H;
   const int bid = blockIdx.x;
@@ -134,7 +140,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   // window value index y of this lane's first accumulator group; the four values of each
   // group are consecutive, read with one 16-byte load from copy (y & 3)
   const int ybase = (MQ - 1) - (QW * wave + ql) + 4 * hh;   // + 32 (kb - qb2) + 8 g
-  const int wcopy = ybase & 3;
+  const int wcopy = ybase & (NCOPY - 1);
 
   // ---- issue the direct loads of key tile j0.  Chunk position p of K / V holds global
   // chunk (row, (p % KCH) ^ swizzle(row)).  Buffer loads: the per-lane part of each address
@@ -150,7 +156,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
     const int row = p / KCH;
     kv_voff[r] = (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
   }
-  auto issue_tile = [&](FwdTile<DH, TW>& tl, int j0) {
+  auto issue_tile = [&](FwdTile<DH, TW, NCOPY>& tl, int j0) {
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       const int p0 = (wave * CPW + r) * 64;
@@ -160,7 +166,9 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
     const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
 #pragma unroll
     for (int r = 0; r < WPW; ++r) {
-      const int x = wave * WPW + r;         // 0 .. 4 * TW / 64 - 1
+      // 0 .. NWL - 1; a wave past the end reloads a segment another wave loads (the same
+      // bytes to the same place), so every wave issues the same number of loads
+      const int x = (wave * WPW + r) % NWL;
       const int cpy = x / (TW / 64), seg = x % (TW / 64);
       lds_dma4(rW, lane * 4, (u0 + cpy + 64 * seg) * 4, &tl.w[cpy][64 * seg]);
     }
@@ -185,7 +193,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   // ---- V is converted from bf16 to fp16 in LDS once per tile, each wave converting the
   // chunks its own direct loads wrote (so it only waits for its own loads), before the
   // barrier that publishes the tile.  P is rounded to fp16 for the PV product.
-  auto convert_v = [&](FwdTile<DH, TW>& tl) {
+  auto convert_v = [&](FwdTile<DH, TW, NCOPY>& tl) {
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       u32x4* pv = (u32x4*)&tl.v[((wave * CPW + r) * 64 + lane) * 8];
@@ -196,14 +204,14 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
     }
   };
   // wait for this wave's loads of tile t + 1 (tile t + 2's may stay in flight), convert it
-  auto convert_next = [&](FwdTile<DH, TW>& nx, int t) {
+  auto convert_next = [&](FwdTile<DH, TW, NCOPY>& nx, int t) {
     if (t + 1 >= ntiles) return;
     if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
     else BAM_WAIT_VMCNT(0);
     convert_v(nx);
   };
 
-  auto compute_tile = [&](const FwdTile<DH, TW>& tl, FwdTile<DH, TW>& nx, int t) {
+  auto compute_tile = [&](const FwdTile<DH, TW, NCOPY>& tl, FwdTile<DH, TW, NCOPY>& nx, int t) {
     const int j0 = jb + t * kNK;
     // A wave whose rows all precede this tile's keys has nothing to do (causal).  Without
     // the mask the second test never holds (tiles end before T), but the branch splits the
@@ -216,21 +224,34 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
     // ---- S'^T = K Q^T + sqrt(Dh) b: each accumulator starts from its bias block (read
     // straight into the accumulator registers), then accumulates the contraction.  All
     // LDS reads of the phase are issued before the first MFMA so their latency overlaps.
-    const f32x4* __restrict__ wv = (const f32x4*)tl.w[wcopy];
     f32x16 sacc[NQB][2];
     u32x4 kw[2][KS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int qb2 = 0; qb2 < NQB; ++qb2) {
-        const int y4 = ((ybase - wcopy) >> 2) + 8 * (kb - qb2);   // 16-byte units
+        if constexpr (NCOPY == 4) {
+          const f32x4* __restrict__ wv = (const f32x4*)tl.w[wcopy];
+          const int y4 = ((ybase - wcopy) >> 2) + 8 * (kb - qb2);   // 16-byte units
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v4 = wv[y4 + 2 * g];
-          sacc[qb2][kb][4 * g + 0] = v4[0];
-          sacc[qb2][kb][4 * g + 1] = v4[1];
-          sacc[qb2][kb][4 * g + 2] = v4[2];
-          sacc[qb2][kb][4 * g + 3] = v4[3];
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v4 = wv[y4 + 2 * g];
+            sacc[qb2][kb][4 * g + 0] = v4[0];
+            sacc[qb2][kb][4 * g + 1] = v4[1];
+            sacc[qb2][kb][4 * g + 2] = v4[2];
+            sacc[qb2][kb][4 * g + 3] = v4[3];
+          }
+        } else {
+          const f32x2* __restrict__ wv = (const f32x2*)tl.w[wcopy];
+          const int y2 = ((ybase - wcopy) >> 1) + 16 * (kb - qb2);   // 8-byte units
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x2 lo = wv[y2 + 4 * g], hi = wv[y2 + 4 * g + 1];
+            sacc[qb2][kb][4 * g + 0] = lo[0];
+            sacc[qb2][kb][4 * g + 1] = lo[1];
+            sacc[qb2][kb][4 * g + 2] = hi[0];
+            sacc[qb2][kb][4 * g + 3] = hi[1];
+          }
         }
       }
       if constexpr (DH == 64) {
