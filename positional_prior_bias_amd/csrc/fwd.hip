@@ -46,18 +46,36 @@ namespace {
 
 constexpr int kNK = 64;    // keys per tile
 
-// Four copies of the reversed distance window, copy c shifted by c entries, so every lane
-// reads its runs of 4 consecutive distances with one aligned 16-byte load.  Copies are
-// TW + 16 floats apart: copy c then starts at 16-byte bank group 4 c, and the 16 lanes of
-// one LDS cycle (4 consecutive groups of 4 lanes, each lane group spanning the 4 copies)
-// hit 16 distinct bank groups.
-template <int DH, int TW, int NCOPY>
+// Copies of the reversed distance window, copy c shifted by c entries, so every lane reads
+// its runs of consecutive distances with aligned 16-byte (4 copies) or 8-byte (2 copies)
+// loads.  Copies are a multiple of 32 floats plus 16 apart: copy c then starts at 16-byte
+// bank group 4 c, and the 16 lanes of one LDS cycle (4 consecutive groups of 4 lanes, each
+// lane group spanning the copies) hit distinct bank groups.
+//
+// With four copies every pipeline buffer holds its tile's whole window (TW entries per copy).
+// With two copies the window lives in one ring shared by the buffers (kRing below): a tile's
+// window is three 64-entry segments, consecutive tiles share two of them, so each tile adds
+// one segment.  WN = floats of window per buffer (0 for the ring).
+template <int DH, int WN>
 struct FwdTile {
   uint16_t k[kNK * DH];
   uint16_t v[kNK * DH];
-  float w[NCOPY][TW + 16];
+  float w[WN];
+};
+template <int DH>
+struct FwdTile<DH, 0> {
+  uint16_t k[kNK * DH];
+  uint16_t v[kNK * DH];
 };
 
+// The ring: segment k of local tile t sits in slot (t + k) & 3 (64 entries each), and slots 0
+// and 1 are mirrored after slot 3, so tile t's window is the 192 contiguous entries from
+// 64 (t & 3).  Per copy 384 entries, copies kRingStride floats apart (400 = 12 * 32 + 16).
+// It keeps a work-group of 128 rows (Dh = 64) at 52,288 bytes of LDS: three fit in a CU's
+// 160 KiB, which the hardware allocates in steps of 1,280 bytes (three per-buffer windows
+// would need 54,144 bytes, and only two would fit).
+constexpr int kRingEntries = 384;
+constexpr int kRingStride = 400;
 
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
@@ -74,16 +92,20 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   // Dh = 64 with one query block per wave (8-byte reads), which keeps the work-group's LDS
   // under a third of the CU's so three work-groups (three waves per SIMD) fit.
   constexpr int NCOPY = (DH == 64 && NQB == 1) ? 2 : 4;
-  constexpr int NWL = NCOPY * (TW / 64);          // window loads per tile (all waves)
-  constexpr int WPW = (NWL + 3) / 4;              // window loads per wave; surplus slots repeat one
-  static_assert(NCOPY == 4 || NWL <= 4 * WPW, "window loads");
-  constexpr int LPT = 2 * CPW + WPW;    // direct-load instructions per wave per tile
+  constexpr bool RING = NCOPY == 2;               // two copies: the window is the shared ring
+  static_assert(!RING || TW == 192, "the ring holds windows of three 64-entry segments");
+  constexpr int WPW = RING ? 1 : NCOPY * (TW / 64) / 4;   // window loads per wave per tile
+  static_assert(RING || NCOPY * (TW / 64) % 4 == 0, "window loads split over four waves");
+  constexpr int KVL = 2 * CPW;          // K / V direct loads per wave per tile
+  constexpr int LPT = KVL + WPW;        // direct-load instructions per wave per tile
   constexpr float kLazy = 8.0f;         // rescale only when a row max grows by > 2^8
   static_assert(kNK * KCH % 256 == 0, "tile must split into 1 KiB wave loads");
   static_assert(LPT < 64, "vmcnt range");
 
   // three buffers as distinct objects: the tile being read, and up to two being filled
-  __shared__ __attribute__((aligned(16))) FwdTile<DH, TW, NCOPY> tA, tB, tC;
+  using Tile = FwdTile<DH, RING ? 0 : NCOPY * (TW + 16)>;
+  __shared__ __attribute__((aligned(16))) Tile tA, tB, tC;
+  __shared__ __attribute__((aligned(16))) float wring[RING ? NCOPY * kRingStride : 4];
 
   const int BH = a.B * a.H;
   const int bid = blockIdx.x;
@@ -156,23 +178,35 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
     const int row = p / KCH;
     kv_voff[r] = (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
   }
-  auto issue_tile = [&](FwdTile<DH, TW, NCOPY>& tl, int j0) {
+  auto issue_tile = [&](Tile& tl, int j0) {
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       const int p0 = (wave * CPW + r) * 64;
       lds_dma16(rK, kv_voff[r] + j0 * DH * 2, 0, &tl.k[p0 * 8]);
       lds_dma16(rV, kv_voff[r] + j0 * DH * 2, 0, &tl.v[p0 * 8]);
     }
-    const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
+    if constexpr (!RING) {
+      const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
 #pragma unroll
-    for (int r = 0; r < WPW; ++r) {
-      // 0 .. NWL - 1; a wave past the end reloads a segment another wave loads (the same
-      // bytes to the same place), so every wave issues the same number of loads
-      const int x = (wave * WPW + r) % NWL;
-      const int cpy = x / (TW / 64), seg = x % (TW / 64);
-      lds_dma4(rW, lane * 4, (u0 + cpy + 64 * seg) * 4, &tl.w[cpy][64 * seg]);
+      for (int r = 0; r < WPW; ++r) {
+        const int x = wave * WPW + r;                 // copy x / (TW / 64), segment x % (TW / 64)
+        const int cpy = x / (TW / 64), seg = x % (TW / 64);
+        lds_dma4(rW, lane * 4, (u0 + cpy + 64 * seg) * 4, &tl.w[cpy * (TW + 16) + 64 * seg]);
+      }
     }
   };
+  // Ring segment k of local tile t (entries from the window start + 64 k) into slot
+  // (t + k) & 3 of copy cpy, and into its mirror if mirror is set and the slot is 0 or 1.
+  // A wave asked for a mirror that does not exist reloads the slot itself (the same bytes to
+  // the same place), so every wave issues the same number of loads.
+  auto ring_load = [&](int t, int k, int cpy, bool mirror) {
+    const int u0 = a.tab_d0 - (i0 + MQ - 1 - (jb + t * kNK));
+    const int slot = (t + k) & 3;
+    const int pos = (mirror && slot < 2) ? 256 + 64 * slot : 64 * slot;
+    lds_dma4(rW, lane * 4, (u0 + cpy + 64 * k) * 4, &wring[cpy * kRingStride + pos]);
+  };
+  // the segment tile t adds (k = 2): one load per wave (copy wave & 1, mirror wave >> 1)
+  auto ring_next = [&](int t) { ring_load(t, 2, wave & 1, wave >> 1); };
 
   // Dh = 64: per-lane LDS byte offsets of the K and V^T operand reads, fixed for the whole
   // kernel.  V^T operand rows r0 = 16 st + rb and r1 = r0 + 8, column 32 db + cq: the row
@@ -193,7 +227,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   // ---- V is converted from bf16 to fp16 in LDS once per tile, each wave converting the
   // chunks its own direct loads wrote (so it only waits for its own loads), before the
   // barrier that publishes the tile.  P is rounded to fp16 for the PV product.
-  auto convert_v = [&](FwdTile<DH, TW, NCOPY>& tl) {
+  auto convert_v = [&](Tile& tl) {
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       u32x4* pv = (u32x4*)&tl.v[((wave * CPW + r) * 64 + lane) * 8];
@@ -204,14 +238,15 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
     }
   };
   // wait for this wave's loads of tile t + 1 (tile t + 2's may stay in flight), convert it
-  auto convert_next = [&](FwdTile<DH, TW, NCOPY>& nx, int t) {
+  auto convert_next = [&](Tile& nx, int t) {
     if (t + 1 >= ntiles) return;
-    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
+    // in flight behind tile t + 1's loads: tile t + 2's (its ring segment is issued later)
+    if (t + 2 < ntiles) BAM_WAIT_VMCNT(RING ? KVL : LPT);
     else BAM_WAIT_VMCNT(0);
     convert_v(nx);
   };
 
-  auto compute_tile = [&](const FwdTile<DH, TW, NCOPY>& tl, FwdTile<DH, TW, NCOPY>& nx, int t) {
+  auto compute_tile = [&](const Tile& tl, Tile& nx, int t) {
     const int j0 = jb + t * kNK;
     // A wave whose rows all precede this tile's keys has nothing to do (causal).  Without
     // the mask the second test never holds (tiles end before T), but the branch splits the
@@ -231,7 +266,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
 #pragma unroll
       for (int qb2 = 0; qb2 < NQB; ++qb2) {
         if constexpr (NCOPY == 4) {
-          const f32x4* __restrict__ wv = (const f32x4*)tl.w[wcopy];
+          const f32x4* __restrict__ wv = (const f32x4*)&tl.w[wcopy * (TW + 16)];
           const int y4 = ((ybase - wcopy) >> 2) + 8 * (kb - qb2);   // 16-byte units
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -242,7 +277,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
             sacc[qb2][kb][4 * g + 3] = v4[3];
           }
         } else {
-          const f32x2* __restrict__ wv = (const f32x2*)tl.w[wcopy];
+          const f32x2* __restrict__ wv = (const f32x2*)&wring[wcopy * kRingStride + 64 * (t & 3)];
           const int y2 = ((ybase - wcopy) >> 1) + 16 * (kb - qb2);   // 8-byte units
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -371,7 +406,18 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   // Q is loaded between the first two tiles with buffer loads the compiler does not track
   // (rows at or beyond T load as zeros), so one wait covers tile 0 and Q and tile 1 stays
   // in flight; the empty asm statements after the wait make Q's registers defined there.
+  // With the ring, tile 0's window (segments 0 .. 2 of both copies and the mirrors of slots
+  // 0 and 1: ten loads, three per wave, the surplus repeating) goes first; each later tile's
+  // segment is issued one tile ahead, after the barrier that frees its slot.
   BAM_WAIT_VMCNT(0);
+  if constexpr (RING) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int x = (wave * 3 + r) % 10;
+      const int idx = x % 5;
+      ring_load(0, idx < 3 ? idx : idx - 3, x / 5, idx >= 3);
+    }
+  }
   issue_tile(tA, jb);
   {
     const i32x4 rQ = buffer_rsrc(Q, (uint32_t)T * DH * 2);
@@ -387,7 +433,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   }
   if (ntiles > 1) {
     issue_tile(tB, jb + kNK);
-    BAM_WAIT_VMCNT(LPT);       // tile 0 and Q landed (tile 1 may be in flight)
+    BAM_WAIT_VMCNT(RING ? KVL : LPT);   // tile 0 and Q landed (tile 1 may be in flight)
   } else {
     BAM_WAIT_VMCNT(0);
   }
@@ -402,16 +448,24 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   BAM_BARRIER_VMCNT(63);       // publish tile 0
   // every wave has waited for its loads of tile t + 1 (in compute_tile); publish it
   auto advance = [&]() { BAM_BARRIER_VMCNT(63); };
+  // tile t's step: issue the ring segment of tile t + 1 (its slot held tile t - 1's first
+  // segment) and the K / V loads of tile t + 2, then compute tile t
+  auto issue_ahead = [&](Tile& tl, int t) {
+    if constexpr (RING) {
+      if (t + 1 < ntiles) ring_next(t + 1);
+    }
+    if (t + 2 < ntiles) issue_tile(tl, jb + (t + 2) * kNK);
+  };
   for (int t = 0; t < ntiles; t += 3) {
-    if (t + 2 < ntiles) issue_tile(tC, jb + (t + 2) * kNK);
+    issue_ahead(tC, t);
     compute_tile(tA, tB, t);
     advance();
     if (t + 1 >= ntiles) break;
-    if (t + 3 < ntiles) issue_tile(tA, jb + (t + 3) * kNK);
+    issue_ahead(tA, t + 1);
     compute_tile(tB, tC, t + 1);
     advance();
     if (t + 2 >= ntiles) break;
-    if (t + 4 < ntiles) issue_tile(tB, jb + (t + 4) * kNK);
+    issue_ahead(tB, t + 2);
     compute_tile(tC, tA, t + 2);
     advance();
   }
