@@ -169,16 +169,24 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // later LDS read wait for all of them, which would drain the prefetch of later tiles.  The
 // caller orders them with BAM_WAIT_VMCNT / BAM_BARRIER_VMCNT (each load counts once).
 // `soff` and `lds_base` must be wave-uniform.
+//
+// Every buffer load written as inline assembly starts with BAM_VMEM_SGPR_NOPS.  Its SGPR
+// operands (the offset, the resource) are often written by v_readfirstlane just before it,
+// and on this architecture a vector-memory instruction that reads an SGPR written by a VALU
+// instruction needs five wait states first; the compiler enforces that for the instructions
+// it emits, but not for inline assembly (a load that read a stale offset returned zeros).
+// The same nops cover the one wait state between writing M0 and an LDS-direct load.
+#define BAM_VMEM_SGPR_NOPS "s_nop 4\n\t"
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 __device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t voff, uint32_t soff, void* lds_base) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile(BAM_VMEM_SGPR_NOPS "buffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(lds_addr(lds_base))
                : "memory");
 }
 __device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t voff, uint32_t soff, void* lds_base) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+  asm volatile(BAM_VMEM_SGPR_NOPS "buffer_load_dword %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(lds_addr(lds_base))
                : "memory");
 }

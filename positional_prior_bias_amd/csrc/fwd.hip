@@ -427,7 +427,8 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint32_t off = (uint32_t)(i * DH + 16 * ks + 8 * hh) * 2u;
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(qw[qb2][ks]) : "v"(off), "s"(rQ) : "memory");
+        asm volatile(BAM_VMEM_SGPR_NOPS "buffer_load_dwordx4 %0, %1, %2, 0 offen"
+                     : "=v"(qw[qb2][ks]) : "v"(off), "s"(rQ) : "memory");
       }
     }
   }
