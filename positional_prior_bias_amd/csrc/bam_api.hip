@@ -313,21 +313,26 @@ bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void*
 
 // ---------------------------------------------------------------------------------------
 namespace {
+// Backward workspace: the four distance tables (forward layout), D, the per-row scalars of
+// the dK / dV kernel (four arrays over rows padded to 64) and the parameter partials.
 struct BwdLayout {
-  size_t tab_off, ta_off, tb_off, tm_off, D_off, part_off, total;
+  size_t tab_off, ta_off, tb_off, tm_off, D_off, rs_off, part_off, total;
+  int Tp;
   TableGeom g;
 };
 
 BwdLayout bwd_layout(int B, int H, int T, bool causal) {
   BwdLayout L;
-  L.g = table_geom(T, causal);
+  L.g = fwd_table_geom(T, causal);
   const size_t tabsz = align_up((size_t)H * L.g.stride * sizeof(float));
+  L.Tp = (T + 63) / 64 * 64;
   L.tab_off = 0;
   L.ta_off = tabsz;
   L.tb_off = 2 * tabsz;
   L.tm_off = 3 * tabsz;
   L.D_off = 4 * tabsz;
-  L.part_off = L.D_off + align_up((size_t)B * H * T * sizeof(float));
+  L.rs_off = L.D_off + align_up((size_t)B * H * T * sizeof(float));
+  L.part_off = L.rs_off + align_up((size_t)4 * B * H * L.Tp * sizeof(float));
   L.total = L.part_off + align_up(bam::bwd_param_partials(B, H, T) * sizeof(float));
   return L;
 }
@@ -364,6 +369,10 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64)) return BAM_EUNSUPPORTED;
   if ((o_dtype != BAM_BF16 && o_dtype != BAM_F32) || (grad_dtype != BAM_BF16 && grad_dtype != BAM_F32))
     return BAM_EUNSUPPORTED;
+  // the dK / dV kernel's buffer loads address one (b, h) of Q / dO and all four row-scalar
+  // arrays with 32-bit byte ranges
+  if ((size_t)T * Dh * 2 > 0x7fffffffu || (size_t)16 * B * H * ((T + 63) / 64 * 64) > 0x7fffffffu)
+    return BAM_EUNSUPPORTED;
   const bool causal = (flags & BAM_CAUSAL) != 0;
   const BwdLayout L = bwd_layout(B, H, T, causal);
   if (workspace_bytes < L.total) return BAM_EWORKSPACE;
@@ -373,8 +382,9 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   float* ta = (float*)(ws + L.ta_off);
   float* tb = (float*)(ws + L.tb_off);
   float* tm = dmu ? (float*)(ws + L.tm_off) : nullptr;
-  hipError_t e = bam::launch_prior_table(alpha, beta, mu, prior_kind(flags), H, L.g.d0, L.g.n,
-                                         L.g.stride, 1.0f, tab, ta, tb, tm, st);
+  hipError_t e = bam::launch_prior_table_ex(alpha, beta, mu, prior_kind(flags), H, L.g.d0, -1, L.g.n,
+                                            L.g.stride, causal ? 0 : -(T - 1), T - 1, std::sqrt((float)Dh),
+                                            tab, ta, tb, tm, st);
   if (e != hipSuccess) return BAM_EHIP;
   bam::BwdArgs a;
   a.q = q;
@@ -397,6 +407,8 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   a.causal = causal;
   a.ssmax = (flags & BAM_SSMAX) != 0;
   a.Dbuf = (float*)(ws + L.D_off);
+  a.rowsc = (float*)(ws + L.rs_off);
+  a.Tp = L.Tp;
   a.dq_acc = nullptr;
   a.param_part = (float*)(ws + L.part_off);
   a.dq = dq;

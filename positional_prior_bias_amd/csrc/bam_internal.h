@@ -108,7 +108,10 @@ struct BwdArgs {
   bool o_f32;
   const float* lse;
   const void* dout;
-  const float* tab;      // bias b(d), index d (causal: 0..T-1; else d + T - 1)
+  // Distance tables in the forward's layout: reversed (entry e holds d = tab_d0 - e) and
+  // padded by kFwdTabPad entries on both sides; tab holds sqrt(Dh) b(d) (-inf padding), the
+  // derivative tables db/dalpha, db/dbeta, db/dmu unscaled (0 padding).
+  const float* tab;
   const float* tab_da;   // db/dalpha
   const float* tab_db;   // db/dbeta
   const float* tab_dm;   // db/dmu (null: dmu not wanted)
@@ -118,6 +121,11 @@ struct BwdArgs {
   int B, H, T;
   bool causal, ssmax;
   float* Dbuf;           // [B,H,T] rowsum(dO * O)
+  // Per-row scalars of the dK / dV kernel, four arrays [B*H][Tp] (Tp = T rounded up to 64):
+  // Cl = c log2(e) / sqrt(Dh), L2 = lse log2(e), D, Cq = c / sqrt(Dh); rows at or beyond T
+  // hold FLT_MIN, +inf, 0, 0 (no weight).
+  float* rowsc;
+  int Tp;
   float* dq_acc;         // [B,H,T,Dh] fp32 accumulator
   float* param_part;     // [nparts][3][H] per-block partial sums (or direct)
   void* dq;

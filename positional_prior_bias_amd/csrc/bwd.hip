@@ -9,18 +9,20 @@
 // Mechanism", "Implementation Details"); the parameter gradients are reduced in fp32.
 //
 // Kernels (all bf16 MFMA 32x32x16, fp32 accumulate, P recomputed from lse):
-//   bwd_pre    D_i = rowsum(dO * O)
+//   bwd_pre    D_i = rowsum(dO * O), and the per-row scalars of bwd_dkdv
 //   bwd_dkdv   a work-group owns 128 keys (32 per wave) and walks the query tiles;
 //              S = Q K^T with queries as MFMA rows and keys as columns puts one key per
 //              lane, so P^T and dZ^T feed dV += P^T dO and dK += dZ^T Q straight from
-//              the accumulators; Q and dO are staged both row-major and transposed.
+//              the accumulators; dO^T and Q^T are transposing LDS reads of the row-major
+//              tiles, which go straight from HBM to LDS, three tiles in flight.
 //   bwd_dq     a work-group owns 128 queries (32 per wave), shaped like the forward
 //              (one query per lane), walks the key tiles: dQ^T += K^T dZ^T, and the
 //              per-element parameter terms are accumulated here, one partial per
 //              work-group (no atomics: the reduction order is fixed).
 //   bwd_params sums the partials of each head (alpha, beta, s and, when wanted, mu).
 // The bias is again the accumulator's initial value (sqrt(Dh) b from the distance
-// window in LDS, -inf where the causal mask forbids the pair).
+// window in LDS, -inf where the causal mask forbids the pair); the tables have the
+// forward's layout (reversed, padded, sqrt(Dh) b).
 #include <float.h>
 
 #include "bam_device.h"
@@ -37,14 +39,21 @@ constexpr int kNK = 64;      // keys per tile (dq)
 constexpr int kTS = 64 + 4;  // transposed-tile row stride (bf16)
 
 // ------------------------------------------------------------------------------------
+// D_i = rowsum(dO * O) over rows padded to 64 (bh * Tp + i), and the per-row scalars of
+// the dK / dV kernel: Cl = c log2(e) / sqrt(Dh), L2 = lse log2(e), D, Cq = c / sqrt(Dh);
+// rows at or beyond T get FLT_MIN, +inf, 0, 0 (their weights are exactly zero).
 template <int DH>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a, long nrows) {
+__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a, long nrows_p) {
   constexpr int LPR = DH / 8;  // lanes per row, 8 elements each
   const long gt = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gt / LPR;
+  const long rowp = gt / LPR;
   const int cl = (int)(gt % LPR);
+  const int bh = (int)(rowp / a.Tp);
+  const int i = (int)(rowp - (long)bh * a.Tp);
+  const bool valid = rowp < nrows_p && i < a.T;
+  const long row = (long)bh * a.T + i;
   float acc = 0.f;
-  if (row < nrows) {
+  if (valid) {
     const size_t off = (size_t)row * DH + cl * 8;
     const u32x4 dw = *(const u32x4*)((const uint16_t*)a.dout + off);
     float ov[8];
@@ -66,24 +75,54 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a, long nrows) {
   }
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < nrows && cl == 0) a.Dbuf[row] = acc;
+  if (rowp < nrows_p && cl == 0) {
+    const size_t n = (size_t)nrows_p;
+    float* rs = a.rowsc + rowp;
+    if (valid) {
+      a.Dbuf[row] = acc;
+      const int h = bh % a.H;
+      const float c = ssmax_c(a.ssmax, a.ssmax ? a.s[h] : 1.0f, a.causal ? i + 1 : a.T);
+      const float isd = 1.0f / __builtin_sqrtf((float)DH);
+      rs[0] = fmaxf(c * kLog2e * isd, FLT_MIN);
+      rs[n] = a.lse[row] * kLog2e;
+      rs[2 * n] = acc;
+      rs[3 * n] = c * isd;
+    } else {
+      rs[0] = FLT_MIN;
+      rs[n] = __builtin_huge_valf();
+      rs[2 * n] = 0.f;
+      rs[3 * n] = 0.f;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------
+// dK, dV.  A work-group owns kKB = 128 keys (32 per wave; lane ql holds key jw + ql as the
+// MFMA column) and walks the query tiles of 64 rows (causal: from its first key on).
+// S = Q K^T and dP = dO V^T have the queries as MFMA rows, so P^T and dZ^T leave the
+// accumulators in the A-operand layout of dV += P^T dO and dK += (c dZ / sqrt(Dh))^T Q (the
+// contraction runs over the queries in the order the accumulator holds them); the B
+// operands dO^T and Q^T are transposing reads of the row-major tiles.
+// A query tile (Q, dO, the distance window and the four per-row scalars) goes straight from
+// HBM to LDS with buffer loads issued from inline assembly; three tiles in flight, one
+// barrier per tile.  Rows at or beyond T load as zeros and carry zero weight.
+template <int DH>
+struct BwdQTile {
+  uint16_t q[kQT * DH];     // swizzled 16-byte chunks, as the forward's K / V tiles
+  uint16_t o[kQT * DH];
+  float w[kQT + kKB];       // sqrt(Dh) b(d) for d = d_max - y (reversed table window)
+  float rs[4][kQT];         // Cl, L2, D, Cq of the tile's rows
+};
+
 template <int DH, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
-  constexpr int TW = kQT + kKB;   // distance window
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kQT * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[DH * kTS];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[kQT * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[DH * kTS];
-  __shared__ float tw[TW];
-  __shared__ __attribute__((aligned(16))) float sCl[kQT];
-  __shared__ __attribute__((aligned(16))) float sL2[kQT];
-  __shared__ __attribute__((aligned(16))) float sD[kQT];
-  __shared__ __attribute__((aligned(16))) float sCq[kQT];
+  constexpr int KCH = DH / 8;                 // 16-byte chunks per row
+  constexpr int CPW = kQT * KCH / 256;        // direct 16-byte loads per wave per tensor
+  constexpr int LPT = 2 * CPW + 2;            // direct loads per wave per tile
+  static_assert(kQT * KCH % 256 == 0 && (kQT + kKB) == 3 * 64, "tile shape");
+  __shared__ __attribute__((aligned(16))) BwdQTile<DH> tA, tB, tC;
 
   const int BH = a.B * a.H;
   const int kb = blockIdx.x / BH;
@@ -98,7 +137,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31;
   const int hh = lane >> 5;
   const int j0 = kb * kKB;
@@ -117,65 +156,99 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
     kf[ks] = as_bf16x8(kw);
     vf[ks] = as_bf16x8(vw);
   }
-
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) { dk[db][x] = 0.f; dv[db][x] = 0.f; }
 
-  const float sqrtD = __builtin_sqrtf((float)DH);
-  const float inv_sqrtD = 1.0f / sqrtD;
-  const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
-  const int dlo = CAUSAL ? 0 : -(T - 1);
-  const int dhi = T - 1;
-  const float sh = a.ssmax ? a.s[h] : 1.0f;
   const int qstart = CAUSAL ? j0 : 0;
+  const int ntiles = (T - qstart + kQT - 1) / kQT;
 
-  for (int i0 = qstart; i0 < T; i0 += kQT) {
-    __syncthreads();
-    stage_rows<DH, kQT, 256>(Q, i0, T, Qs, tid);
-    stage_rows<DH, kQT, 256>(dO, i0, T, dOs, tid);
-    stage_rows_T<DH, kQT, 256, kTS>(Q, i0, T, Qt, tid);
-    stage_rows_T<DH, kQT, 256, kTS>(dO, i0, T, dOt, tid);
-    const int d_min = i0 - j0 - (kKB - 1);
-    for (int x = tid; x < TW; x += 256) {
-      const int d = d_min + x;
-      tw[x] = (d >= dlo && d <= dhi) ? sqrtD * tabh[d - a.tab_d0] : kNegInf;
+  // direct loads: chunk position p of a tile holds global chunk (row, (p % KCH) ^ swizzle(row))
+  const i32x4 rQ = buffer_rsrc(Q, (uint32_t)T * DH * 2);
+  const i32x4 rO = buffer_rsrc(dO, (uint32_t)T * DH * 2);
+  const i32x4 rW = buffer_rsrc(a.tab + (size_t)h * a.tab_stride, (uint32_t)a.tab_stride * 4);
+  const uint32_t nrs = (uint32_t)BH * a.Tp;   // rows per scalar array
+  const i32x4 rR = buffer_rsrc(a.rowsc + (size_t)bh * a.Tp, (3u * nrs + (uint32_t)a.Tp) * 4u);
+  int voff[CPW];
+#pragma unroll
+  for (int r = 0; r < CPW; ++r) {
+    const int p = (wave * CPW + r) * 64 + lane;
+    const int row = p / KCH;
+    voff[r] = (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
+  }
+  auto issue_tile = [&](BwdQTile<DH>& tl, int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < CPW; ++r) {
+      const int p0 = (wave * CPW + r) * 64;
+      lds_dma16(rQ, voff[r] + i0 * DH * 2, 0, &tl.q[p0 * 8]);
+      lds_dma16(rO, voff[r] + i0 * DH * 2, 0, &tl.o[p0 * 8]);
     }
-    if (tid < kQT) {
-      const int i = i0 + tid;
-      if (i < T) {
-        const int n = CAUSAL ? i + 1 : T;
-        const float c = ssmax_c(a.ssmax, sh, n);
-        sCl[tid] = fmaxf(c * kLog2e * inv_sqrtD, FLT_MIN);
-        sL2[tid] = a.lse[(size_t)bh * T + i] * kLog2e;
-        sD[tid] = a.Dbuf[(size_t)bh * T + i];
-        sCq[tid] = c * inv_sqrtD;
-      } else {
-        sCl[tid] = FLT_MIN;
-        sL2[tid] = __builtin_huge_valf();
-        sD[tid] = 0.f;
-        sCq[tid] = 0.f;
-      }
+    // the window (three 64-entry segments from the entry of d_max = i0 + kQT - 1 - j0) and
+    // the four row-scalar arrays: seven 256-byte loads, two per wave (the eighth repeats one)
+    const int e0 = a.tab_d0 - (i0 + kQT - 1 - j0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int x = min(2 * wave + r, 6);
+      if (x < 3) lds_dma4(rW, lane * 4, (e0 + 64 * x) * 4, &tl.w[64 * x]);
+      else lds_dma4(rR, lane * 4, ((uint32_t)(x - 3) * nrs + (uint32_t)i0) * 4u, &tl.rs[x - 3][0]);
     }
-    __syncthreads();
-    if (CAUSAL && i0 + kQT - 1 < jw) continue;  // every query of the tile precedes this wave's keys
+  };
 
+  // LDS byte offsets of the operand reads.  A operands of S and dP: row 32 qb + ql of the Q /
+  // dO tile, chunk 2 ks + hh.  B operands of dV and dK (transposing reads, as the forward's
+  // V^T): lane (column dh, half hh) holds rows {16 st + 4 hh + 0..3, + 8 .. + 11}.
+  int aOff[KS], vA = 0, vB = 0;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aOff[ks] = 2 * (ql * DH + ((2 * ks + hh) ^ vswz<DH>(ql)) * 8);
+  const int G = lane >> 4, gi = lane & 15;
+  if constexpr (DH == 64) {
+    const int rb = 4 * (G >> 1) + (gi >> 2);
+    const int ch0 = (2 * (G & 1) + ((gi & 3) >> 1)) ^ vswz<DH>(rb);
+    vA = 128 * rb + 16 * ch0 + 8 * (gi & 1);
+    vB = 128 * rb + 16 * (ch0 ^ 4) + 8 * (gi & 1);
+  }
+  auto t_operand = [&](const uint16_t* tile, int db, int st) __attribute__((always_inline)) {
+    s16x4 v0, v1;
+    if constexpr (DH == 64) {
+      const char* tv = (const char*)tile;
+      v0 = lds_read_tr16((const uint16_t*)(tv + (db ? vB : vA) + 2048 * st));
+      v1 = lds_read_tr16((const uint16_t*)(tv + (db ? vA : vB) + 2048 * st + 1024));
+    } else {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (gi & 3);
+      const int r0 = 16 * st + 4 * (G >> 1) + (gi >> 2);
+      const int r1 = r0 + 8;
+      v0 = lds_read_tr16(&tile[r0 * DH + (((col >> 3) ^ vswz<DH>(r0)) << 3) + (col & 7)]);
+      v1 = lds_read_tr16(&tile[r1 * DH + (((col >> 3) ^ vswz<DH>(r1)) << 3) + (col & 7)]);
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, vv);
+  };
+
+  auto compute = [&](const BwdQTile<DH>& tl, int i0) __attribute__((always_inline)) {
+    // Causal: every query of the tile precedes this wave's keys.  Otherwise the second test
+    // never holds (tiles start before T), but the branch keeps the tile a scheduling region
+    // of its own, as in the causal case (one region with the loop around it needs more
+    // registers than two waves per SIMD have).
+    if ((CAUSAL && i0 + kQT - 1 < jw) || (!CAUSAL && i0 >= T)) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // S' = Q K^T + sqrt(Dh) b (queries as rows), dP = dO V^T
+      __builtin_amdgcn_sched_barrier(0);
+      // S' = Q K^T + sqrt(Dh) b (queries as rows), dP = dO V^T.  Window index of query row
+      // qrow and key 32 wave + ql: y = kQT - 1 - qrow + 32 wave + ql.
       f32x16 s, dp;
+      const int ybase = kQT - 1 + 32 * wave + ql - 32 * qb - 4 * hh;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int qrow = 32 * qb + 8 * (x >> 2) + 4 * hh + (x & 3);
-        s[x] = tw[qrow - 32 * wave - ql + (kKB - 1)];
+        s[x] = tl.w[ybase - 8 * (x >> 2) - (x & 3)];
         dp[x] = 0.f;
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 qw = read_chunk<DH>(Qs, 32 * qb + ql, 2 * ks + hh);
-        const u32x4 ow = read_chunk<DH>(dOs, 32 * qb + ql, 2 * ks + hh);
+        const u32x4 qw = *(const u32x4*)((const char*)tl.q + aOff[ks] + 64 * DH * qb);
+        const u32x4 ow = *(const u32x4*)((const char*)tl.o + aOff[ks] + 64 * DH * qb);
         s = mfma32x32x16(as_bf16x8(qw), kf[ks], s);
         dp = mfma32x32x16(as_bf16x8(ow), vf[ks], dp);
       }
@@ -187,10 +260,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int q4 = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 cl4 = *(const f32x4*)(sCl + q4);
-        const f32x4 l24 = *(const f32x4*)(sL2 + q4);
-        const f32x4 d4 = *(const f32x4*)(sD + q4);
-        const f32x4 cq4 = *(const f32x4*)(sCq + q4);
+        const f32x4 cl4 = *(const f32x4*)&tl.rs[0][q4];
+        const f32x4 l24 = *(const f32x4*)&tl.rs[1][q4];
+        const f32x4 d4 = *(const f32x4*)&tl.rs[2][q4];
+        const f32x4 cq4 = *(const f32x4*)&tl.rs[3][q4];
         float pv[4], zv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -199,24 +272,55 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
           pv[r] = p;
           zv[r] = p * (dp[x] - d4[r]) * cq4[r];
         }
-        // register x = 8 s' + t, t = 4 (g & 1) + r  ->  operand st = s', dwords (t >> 1)
+        // register x = 8 s' + t, t = 4 (g & 1) + r  ->  operand s', dwords (t >> 1)
         pf[g >> 1][2 * (g & 1) + 0] = pack_bf16x2(pv[0], pv[1]);
         pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(pv[2], pv[3]);
         zf[g >> 1][2 * (g & 1) + 0] = pack_bf16x2(zv[0], zv[1]);
         zf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(zv[2], zv[3]);
       }
       // dV += P^T dO, dK += (c dZ / sqrt(Dh))^T Q   (contraction over this block's queries)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int row = 32 * db + ql;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-          const int col = 32 * qb + 16 * sp + 4 * hh;
-          dv[db] = mfma32x32x16(as_bf16x8(pf[sp]), read_T_operand<kTS>(dOt, row, col), dv[db]);
-          dk[db] = mfma32x32x16(as_bf16x8(zf[sp]), read_T_operand<kTS>(Qt, row, col), dk[db]);
+          dv[db] = mfma32x32x16(as_bf16x8(pf[sp]), t_operand(tl.o, db, 2 * qb + sp), dv[db]);
+          dk[db] = mfma32x32x16(as_bf16x8(zf[sp]), t_operand(tl.q, db, 2 * qb + sp), dk[db]);
         }
-      }
     }
+  };
+
+  // three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load; each wave
+  // waits for its own loads of tile t + 1, then the barrier publishes it
+  auto wait_next = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 >= ntiles) return;
+    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
+    else BAM_WAIT_VMCNT(0);
+  };
+  BAM_WAIT_VMCNT(0);
+  issue_tile(tA, qstart);
+  if (ntiles > 1) {
+    issue_tile(tB, qstart + kQT);
+    BAM_WAIT_VMCNT(LPT);
+  } else {
+    BAM_WAIT_VMCNT(0);
+  }
+  BAM_BARRIER_VMCNT(63);       // publish tile 0
+  for (int t = 0; t < ntiles; t += 3) {
+    if (t + 2 < ntiles) issue_tile(tC, qstart + (t + 2) * kQT);
+    compute(tA, qstart + t * kQT);
+    wait_next(t);
+    BAM_BARRIER_VMCNT(63);
+    if (t + 1 >= ntiles) break;
+    if (t + 3 < ntiles) issue_tile(tA, qstart + (t + 3) * kQT);
+    compute(tB, qstart + (t + 1) * kQT);
+    wait_next(t + 1);
+    BAM_BARRIER_VMCNT(63);
+    if (t + 2 >= ntiles) break;
+    if (t + 4 < ntiles) issue_tile(tB, qstart + (t + 4) * kQT);
+    compute(tC, qstart + (t + 2) * kQT);
+    wait_next(t + 2);
+    BAM_BARRIER_VMCNT(63);
   }
 
   // write dK, dV: lane holds head-dim column 32 db + ql of keys jw + 8 (x>>2) + 4 hh + (x&3)
@@ -308,8 +412,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const float* __restrict__ tabah = a.tab_da + (size_t)h * a.tab_stride;
   const float* __restrict__ tabbh = a.tab_db + (size_t)h * a.tab_stride;
   const float* __restrict__ tabmh = MU ? a.tab_dm + (size_t)h * a.tab_stride : nullptr;
-  const int dlo = CAUSAL ? 0 : -(T - 1);
-  const int dhi = T - 1;
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * kNK;
@@ -317,14 +419,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     stage_rows<DH, kNK, 256>(K, j0, T, Ks, tid);
     stage_rows<DH, kNK, 256>(V, j0, T, Vs, tid);
     stage_rows_T<DH, kNK, 256, kTS>(K, j0, T, Kt, tid);
-    const int d_min = i0 - j0 - (kNK - 1);
+    // window entry x holds distance d_min + x (the padded tables hold -inf / 0 outside
+    // the visible distances, and every window lies inside the padding)
+    const int e_min = a.tab_d0 - (i0 - j0 - (kNK - 1));
     for (int x = tid; x < TW; x += 256) {
-      const int d = d_min + x;
-      const bool ok = d >= dlo && d <= dhi;
-      tw[x] = ok ? sqrtD * tabh[d - a.tab_d0] : kNegInf;
-      twa[x] = ok ? tabah[d - a.tab_d0] : 0.f;
-      twb[x] = ok ? tabbh[d - a.tab_d0] : 0.f;
-      if (MU) twm[x] = ok ? tabmh[d - a.tab_d0] : 0.f;
+      tw[x] = tabh[e_min - x];
+      twa[x] = tabah[e_min - x];
+      twb[x] = tabbh[e_min - x];
+      if (MU) twm[x] = tabmh[e_min - x];
     }
     __syncthreads();
 
@@ -430,10 +532,10 @@ __global__ void __launch_bounds__(64) bwd_params_kernel(BwdArgs a, int nper) {
 
 template <int DH, bool CAUSAL>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-  const long nrows = (long)a.B * a.H * a.T;
-  const long pre_threads = nrows * (DH / 8);
+  const long nrows_p = (long)a.B * a.H * a.Tp;
+  const long pre_threads = nrows_p * (DH / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<DH>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
-                     a, nrows);
+                     a, nrows_p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (a.T + kKB - 1) / kKB;
