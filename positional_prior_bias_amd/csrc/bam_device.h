@@ -90,63 +90,9 @@ __device__ __forceinline__ float max_xor32(float x) {
 }
 
 // XOR swizzle (Gray code of the row) of the 16-byte chunks of a row-major bf16 tile in
-// LDS, so 16-byte reads of one chunk column across consecutive rows spread over banks.
+// LDS, so 16-byte reads of one chunk column across consecutive rows spread over banks
+// (the row swizzle of head sizes other than 64, below).
 __device__ __forceinline__ int swz_chunk(int r, int mask) { return (r ^ (r >> 1)) & mask; }
-
-// Stage ROWS rows x DH bf16 (rows row0 .. row0 + ROWS - 1 of a [*, DH] tensor; rows at or
-// beyond nvalid are zero) into LDS row-major with swizzled 16-byte chunks.
-template <int DH, int ROWS, int NT>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int row0, int nvalid,
-                                           uint16_t* dst, int tid) {
-  constexpr int KCH = DH / 8;
-  for (int cidx = tid; cidx < ROWS * KCH; cidx += NT) {
-    const int r = cidx / KCH;
-    const int ch = cidx - r * KCH;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (row0 + r < nvalid) val = *(const u32x4*)(src + (size_t)(row0 + r) * DH + ch * 8);
-    *(u32x4*)(dst + r * DH + (ch ^ swz_chunk(r, KCH - 1)) * 8) = val;
-  }
-}
-
-// 16-byte read of chunk `ch` of row `r` from a tile staged by stage_rows.
-template <int DH>
-__device__ __forceinline__ u32x4 read_chunk(const uint16_t* tile, int r, int ch) {
-  return *(const u32x4*)(tile + r * DH + (ch ^ swz_chunk(r, DH / 8 - 1)) * 8);
-}
-
-// Stage ROWS rows x DH bf16 transposed into LDS: dst[e * STRIDE + r] = src[row0 + r][e]
-// (zero for rows at or beyond nvalid).  Two rows are packed per 32-bit LDS write.
-template <int DH, int ROWS, int NT, int STRIDE>
-__device__ __forceinline__ void stage_rows_T(const uint16_t* __restrict__ src, int row0, int nvalid,
-                                             uint16_t* dst, int tid) {
-  constexpr int KCH = DH / 8;
-  for (int pidx = tid; pidx < (ROWS / 2) * KCH; pidx += NT) {
-    const int p = pidx % (ROWS / 2);
-    const int ch = pidx / (ROWS / 2);
-    const int r0 = 2 * p;
-    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-    if (row0 + r0 < nvalid) v0 = *(const u32x4*)(src + (size_t)(row0 + r0) * DH + ch * 8);
-    if (row0 + r0 + 1 < nvalid) v1 = *(const u32x4*)(src + (size_t)(row0 + r0 + 1) * DH + ch * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = v0[e >> 1], w1 = v1[e >> 1];
-      const uint32_t packed = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                      : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-      *(uint32_t*)(dst + (ch * 8 + e) * STRIDE + r0) = packed;
-    }
-  }
-}
-
-// MFMA operand of 8 bf16 whose contraction index runs over rows {c, c+1, c+2, c+3,
-// c+8, .., c+11} of column `row` of a transposed tile (the order in which a 32x32
-// accumulator holds them in one lane half).
-template <int STRIDE>
-__device__ __forceinline__ bf16x8 read_T_operand(const uint16_t* tileT, int row, int col) {
-  const u32x2 lo = *(const u32x2*)(tileT + row * STRIDE + col);
-  const u32x2 hi = *(const u32x2*)(tileT + row * STRIDE + col + 8);
-  const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-  return as_bf16x8(av);
-}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define BAM_LDS(p) ((__attribute__((address_space(3))) void*)(p))

@@ -36,7 +36,6 @@ constexpr int kQT = 64;      // queries per tile (dkdv)
 constexpr int kKB = 128;     // keys per work-group (dkdv)
 constexpr int kMQ = 128;     // queries per work-group (dq)
 constexpr int kNK = 64;      // keys per tile (dq)
-constexpr int kTS = 64 + 4;  // transposed-tile row stride (bf16)
 
 // ------------------------------------------------------------------------------------
 // D_i = rowsum(dO * O) over rows padded to 64 (bh * Tp + i), and the per-row scalars of
@@ -343,19 +342,32 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
 }
 
 // ------------------------------------------------------------------------------------
+// dQ and the per-element parameter terms.  A work-group owns kMQ = 128 queries (32 per
+// wave, one query per lane as the MFMA column, shaped like the forward) and walks the key
+// tiles of 64.  S^T = K Q^T and dP^T = V dO^T put the keys on the MFMA rows, so dZ^T leaves
+// the accumulators in the B-operand layout of dQ^T += K^T dZ^T; K^T is a transposing read of
+// the row-major K tile.  A key tile (K, V and the windows of the bias and derivative tables)
+// goes straight from HBM to LDS, three tiles in flight, one barrier per tile.
 // MU: also accumulate the offset term c dZ db/dmu (db/dmu table tab_dm).
+template <int DH>
+struct BwdKTile {
+  uint16_t k[kNK * DH];     // swizzled 16-byte chunks, as the forward's K / V tiles
+  uint16_t v[kNK * DH];
+  float w[4][kMQ + kNK];    // sqrt(Dh) b, db/dalpha, db/dbeta, db/dmu at d = d_max - y
+};
+
 template <int DH, bool CAUSAL, bool MU>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
-  constexpr int TW = kMQ + kNK;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kNK * DH];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[DH * kTS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kNK * DH];
-  __shared__ float tw[TW];
-  __shared__ float twa[TW];
-  __shared__ float twb[TW];
-  __shared__ float twm[MU ? TW : 1];
+  constexpr int KCH = DH / 8;
+  constexpr int CPW = kNK * KCH / 256;        // direct 16-byte loads per wave per tensor
+  constexpr int NTAB = MU ? 4 : 3;            // tables whose windows are loaded
+  constexpr int NWL = 3 * NTAB;               // 64-entry window loads per tile (all waves)
+  constexpr int WPW = (NWL + 3) / 4;          // per wave; surplus slots repeat the last load
+  constexpr int LPT = 2 * CPW + WPW;          // direct loads per wave per tile
+  static_assert(kNK * KCH % 256 == 0 && kMQ + kNK == 3 * 64, "tile shape");
+  __shared__ __attribute__((aligned(16))) BwdKTile<DH> tA, tB, tC;
   __shared__ float red[4][4];
 
   const int BH = a.B * a.H;
@@ -372,7 +384,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31;
   const int hh = lane >> 5;
   const int i0 = qb * kMQ;
@@ -408,43 +420,99 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
 
   const int kend = CAUSAL ? min(T, i0 + kMQ) : T;
   const int ntiles = (kend + kNK - 1) / kNK;
-  const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
-  const float* __restrict__ tabah = a.tab_da + (size_t)h * a.tab_stride;
-  const float* __restrict__ tabbh = a.tab_db + (size_t)h * a.tab_stride;
-  const float* __restrict__ tabmh = MU ? a.tab_dm + (size_t)h * a.tab_stride : nullptr;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * kNK;
-    __syncthreads();
-    stage_rows<DH, kNK, 256>(K, j0, T, Ks, tid);
-    stage_rows<DH, kNK, 256>(V, j0, T, Vs, tid);
-    stage_rows_T<DH, kNK, 256, kTS>(K, j0, T, Kt, tid);
-    // window entry x holds distance d_min + x (the padded tables hold -inf / 0 outside
-    // the visible distances, and every window lies inside the padding)
-    const int e_min = a.tab_d0 - (i0 - j0 - (kNK - 1));
-    for (int x = tid; x < TW; x += 256) {
-      tw[x] = tabh[e_min - x];
-      twa[x] = tabah[e_min - x];
-      twb[x] = tabbh[e_min - x];
-      if (MU) twm[x] = tabmh[e_min - x];
+  // direct loads: chunk position p of a tile holds global chunk (row, (p % KCH) ^ swizzle(row))
+  const i32x4 rK = buffer_rsrc(K, (uint32_t)T * DH * 2);
+  const i32x4 rV = buffer_rsrc(V, (uint32_t)T * DH * 2);
+  const size_t hoff = (size_t)h * a.tab_stride;
+  const uint32_t tbytes = (uint32_t)a.tab_stride * 4;
+  const i32x4 rT0 = buffer_rsrc(a.tab + hoff, tbytes);
+  const i32x4 rT1 = buffer_rsrc(a.tab_da + hoff, tbytes);
+  const i32x4 rT2 = buffer_rsrc(a.tab_db + hoff, tbytes);
+  const i32x4 rT3 = buffer_rsrc((MU ? a.tab_dm : a.tab_db) + hoff, tbytes);
+  int voff[CPW];
+#pragma unroll
+  for (int r = 0; r < CPW; ++r) {
+    const int p = (wave * CPW + r) * 64 + lane;
+    const int row = p / KCH;
+    voff[r] = (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
+  }
+  auto issue_tile = [&](BwdKTile<DH>& tl, int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < CPW; ++r) {
+      const int p0 = (wave * CPW + r) * 64;
+      lds_dma16(rK, voff[r] + j0 * DH * 2, 0, &tl.k[p0 * 8]);
+      lds_dma16(rV, voff[r] + j0 * DH * 2, 0, &tl.v[p0 * 8]);
     }
-    __syncthreads();
+    // table windows: three 64-entry segments each from the entry of d_max = i0 + kMQ - 1 - j0
+    const int e0 = a.tab_d0 - (i0 + kMQ - 1 - j0);
+#pragma unroll
+    for (int r = 0; r < WPW; ++r) {
+      const int x = min(wave * WPW + r, NWL - 1);
+      const int tb = x / 3, seg = x - 3 * tb;
+      const uint32_t so = (uint32_t)(e0 + 64 * seg) * 4u;
+      float* dst = &tl.w[tb][64 * seg];
+      if (tb == 0) lds_dma4(rT0, lane * 4, so, dst);
+      else if (tb == 1) lds_dma4(rT1, lane * 4, so, dst);
+      else if (tb == 2) lds_dma4(rT2, lane * 4, so, dst);
+      else lds_dma4(rT3, lane * 4, so, dst);
+    }
+  };
 
+  // LDS byte offsets of the operand reads.  A operands of S^T and dP^T: row 32 kb + ql of the
+  // K / V tile, chunk 2 ks + hh.  A operand of dQ^T (transposing reads, as the forward's V^T):
+  // lane (row dh, half hh) holds keys {16 st + 4 hh + 0..3, + 8 .. + 11} of column dh.
+  int aOff[KS], vA = 0, vB = 0;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aOff[ks] = 2 * (ql * DH + ((2 * ks + hh) ^ vswz<DH>(ql)) * 8);
+  const int G = lane >> 4, gi = lane & 15;
+  if constexpr (DH == 64) {
+    const int rb = 4 * (G >> 1) + (gi >> 2);
+    const int ch0 = (2 * (G & 1) + ((gi & 3) >> 1)) ^ vswz<DH>(rb);
+    vA = 128 * rb + 16 * ch0 + 8 * (gi & 1);
+    vB = 128 * rb + 16 * (ch0 ^ 4) + 8 * (gi & 1);
+  }
+  auto t_operand = [&](const uint16_t* tile, int db, int st) __attribute__((always_inline)) {
+    s16x4 v0, v1;
+    if constexpr (DH == 64) {
+      const char* tv = (const char*)tile;
+      v0 = lds_read_tr16((const uint16_t*)(tv + (db ? vB : vA) + 2048 * st));
+      v1 = lds_read_tr16((const uint16_t*)(tv + (db ? vA : vB) + 2048 * st + 1024));
+    } else {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (gi & 3);
+      const int r0 = 16 * st + 4 * (G >> 1) + (gi >> 2);
+      const int r1 = r0 + 8;
+      v0 = lds_read_tr16(&tile[r0 * DH + (((col >> 3) ^ vswz<DH>(r0)) << 3) + (col & 7)]);
+      v1 = lds_read_tr16(&tile[r1 * DH + (((col >> 3) ^ vswz<DH>(r1)) << 3) + (col & 7)]);
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    return __builtin_bit_cast(bf16x8, vv);
+  };
+
+  auto compute = [&](const BwdKTile<DH>& tl, int j0) __attribute__((always_inline)) {
+    // Causal: every key of the tile follows this wave's queries.  Otherwise the second test
+    // never holds; the branch keeps the tile a scheduling region of its own.
+    if ((CAUSAL && j0 > i0 + 32 * wave + 31) || (!CAUSAL && j0 >= T)) return;
     u32x4 zf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      __builtin_amdgcn_sched_barrier(0);
+      // S'^T = K Q^T + sqrt(Dh) b, dP^T = V dO^T.  Window index of key row kl and this lane's
+      // query: y = kMQ - 1 - (32 wave + ql) + kl.
+      const int ybase = kMQ - 1 - 32 * wave - ql + 32 * kb + 4 * hh;
       f32x16 s, dp;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int kl = 32 * kb + 8 * (x >> 2) + 4 * hh + (x & 3);
-        s[x] = tw[32 * wave + ql + (kNK - 1) - kl];
+        s[x] = tl.w[0][ybase + 8 * (x >> 2) + (x & 3)];
         dp[x] = 0.f;
       }
-      const int r = 32 * kb + ql;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32x32x16(as_bf16x8(read_chunk<DH>(Ks, r, 2 * ks + hh)), qf[ks], s);
-        dp = mfma32x32x16(as_bf16x8(read_chunk<DH>(Vs, r, 2 * ks + hh)), of[ks], dp);
+        const u32x4 kw = *(const u32x4*)((const char*)tl.k + aOff[ks] + 64 * DH * kb);
+        const u32x4 vw = *(const u32x4*)((const char*)tl.v + aOff[ks] + 64 * DH * kb);
+        s = mfma32x32x16(as_bf16x8(kw), qf[ks], s);
+        dp = mfma32x32x16(as_bf16x8(vw), of[ks], dp);
       }
       float zv[16];
 #pragma unroll
@@ -455,24 +523,54 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
         const float p = exp2_fast(Cl * sx - L2);
         const float z = p * (dp[x] - Di);
         zv[x] = z;
-        const int widx = 32 * wave + ql + (kNK - 1) - kl;
+        const int y = ybase + 8 * (x >> 2) + (x & 3);
         const float cz = c * z;
-        ga = fmaf(cz, twa[widx], ga);
-        gb = fmaf(cz, twb[widx], gb);
-        if (MU) gm = fmaf(cz, twm[widx], gm);
+        ga = fmaf(cz, tl.w[1][y], ga);
+        gb = fmaf(cz, tl.w[2][y], gb);
+        if (MU) gm = fmaf(cz, tl.w[3][y], gm);
         gs = fmaf(z * lnn_sd, fmaxf(sx, -FLT_MAX), gs);
       }
 #pragma unroll
       for (int x = 0; x < 16; x += 2) zf[2 * kb + (x >> 3)][(x & 7) >> 1] = pack_bf16x2(zv[x], zv[x + 1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // dQ^T += K^T dZ^T
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int row = 32 * db + ql;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        dq[db] = mfma32x32x16(read_T_operand<kTS>(Kt, row, 16 * st + 4 * hh), as_bf16x8(zf[st]), dq[db]);
-    }
+      for (int st = 0; st < 4; ++st) dq[db] = mfma32x32x16(t_operand(tl.k, db, st), as_bf16x8(zf[st]), dq[db]);
+  };
+
+  // three-stage pipeline, as the dK / dV kernel
+  auto wait_next = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 >= ntiles) return;
+    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
+    else BAM_WAIT_VMCNT(0);
+  };
+  BAM_WAIT_VMCNT(0);
+  issue_tile(tA, 0);
+  if (ntiles > 1) {
+    issue_tile(tB, kNK);
+    BAM_WAIT_VMCNT(LPT);
+  } else {
+    BAM_WAIT_VMCNT(0);
+  }
+  BAM_BARRIER_VMCNT(63);       // publish tile 0
+  for (int t = 0; t < ntiles; t += 3) {
+    if (t + 2 < ntiles) issue_tile(tC, (t + 2) * kNK);
+    compute(tA, t * kNK);
+    wait_next(t);
+    BAM_BARRIER_VMCNT(63);
+    if (t + 1 >= ntiles) break;
+    if (t + 3 < ntiles) issue_tile(tA, (t + 3) * kNK);
+    compute(tB, (t + 1) * kNK);
+    wait_next(t + 1);
+    BAM_BARRIER_VMCNT(63);
+    if (t + 2 >= ntiles) break;
+    if (t + 4 < ntiles) issue_tile(tB, (t + 4) * kNK);
+    compute(tC, (t + 2) * kNK);
+    wait_next(t + 2);
+    BAM_BARRIER_VMCNT(63);
   }
 
   if (valid) {
