@@ -110,6 +110,12 @@ def test_decode_and_bwd_reject_bad_arguments(L):
     st = L.bam_attn_bwd(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 64, 16, 16, None, 16, 3, 16, 16, 16, 0,
                         None, 16, 16, 256, 1 << 20, None)
     assert st == 1                                 # dalpha NULL
+    st = L.bam_attn_bwd(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 1 << 24, 64, 16, 16, None, 16, 3, 16, 16, 16, 0,
+                        16, 16, 16, 256, 1 << 20, None)
+    assert st == 2                                 # one head's Q beyond a 32-bit byte range
+    st = L.bam_attn_bwd(16, 16, 16, 16, 1, 16, 16, 0, 1 << 21, 1, 64, 64, 16, 16, None, 16, 3, 16, 16, 16, 0,
+                        16, 16, 16, 256, 1 << 20, None)
+    assert st == 2                                 # per-row scalars beyond a 32-bit byte range
     assert L.bam_prior_table(None, 16, None, 1, 0, 8, 16, None, None, None) == 1
     st = L.bam_attn_bwd_ex(16, 16, 16, 16, 1, 16, 16, 0, 1, 1, 8, 64, 16, 16, None, 16, 3 | 8, 16, 16, 16, 0,
                            None, 16, 16, 16, 256, 1 << 20, None)
