@@ -12,8 +12,9 @@
 //     Dh = 64 with short sequences (finer work-groups balance the causal triangle), a wave
 //     owns one 32-row block and a work-group 128 rows.
 //   * Key tiles of 64 go straight from HBM to LDS (buffer loads to LDS, issued from inline
-//     assembly so the compiler does not make every LDS read wait for them), three tiles in
-//     flight, one barrier per tile; rows at or beyond T load as zeros.
+//     assembly so the compiler does not make every LDS read wait for them), two tiles in
+//     flight ahead of the one being computed (one for 128-row work-groups with Dh = 64), one
+//     barrier per tile; rows at or beyond T load as zeros.
 //   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) with keys as MFMA rows and queries as
 //     columns: each lane owns one query and 16 keys per 32x32 block, so the row max / sum
 //     of the softmax is an in-lane reduction plus one exchange with lane ^ 32.
@@ -36,6 +37,7 @@
 //   * With a skipping plan (causal only), a work-group starts its key loop at the first
 //     key tile whose weights float32 can still hold (the bound is in skip.hip).
 #include <float.h>
+#include <type_traits>
 
 #include "bam_device.h"
 #include "bam_internal.h"
@@ -102,9 +104,12 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   static_assert(kNK * KCH % 256 == 0, "tile must split into 1 KiB wave loads");
   static_assert(LPT < 64, "vmcnt range");
 
-  // three buffers as distinct objects: the tile being read, and up to two being filled
+  // the buffers as distinct objects: the tile being read, and one (ring) or two being filled
   using Tile = FwdTile<DH, RING ? 0 : NCOPY * (TW + 16)>;
-  __shared__ __attribute__((aligned(16))) Tile tA, tB, tC;
+  __shared__ __attribute__((aligned(16))) Tile tA, tB;
+  typedef typename std::conditional<RING, uint32_t[4], Tile>::type ThirdTile;   // unused with the ring
+  __shared__ __attribute__((aligned(16))) ThirdTile tCst;
+  Tile& tC = *reinterpret_cast<Tile*>(&tCst);
   __shared__ __attribute__((aligned(16))) float wring[RING ? NCOPY * kRingStride : 4];
 
   const int BH = a.B * a.H;
@@ -240,9 +245,12 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   // wait for this wave's loads of tile t + 1 (tile t + 2's may stay in flight), convert it
   auto convert_next = [&](Tile& nx, int t) {
     if (t + 1 >= ntiles) return;
-    // in flight behind tile t + 1's loads: tile t + 2's (its ring segment is issued later)
-    if (t + 2 < ntiles) BAM_WAIT_VMCNT(RING ? KVL : LPT);
-    else BAM_WAIT_VMCNT(0);
+    if constexpr (RING) {
+      BAM_WAIT_VMCNT(0);          // two stages: only tile t + 1's loads are in flight
+    } else {
+      if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);   // tile t + 2's stay in flight
+      else BAM_WAIT_VMCNT(0);
+    }
     convert_v(nx);
   };
 
@@ -400,12 +408,12 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
     }
   };
 
-  // ---- three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load.  Q is
-  // in registers before the first tile load is issued (the compiler would otherwise wait
-  // for it, and so for every load in flight, inside the loop).
-  // Q is loaded between the first two tiles with buffer loads the compiler does not track
-  // (rows at or beyond T load as zeros), so one wait covers tile 0 and Q and tile 1 stays
-  // in flight; the empty asm statements after the wait make Q's registers defined there.
+  // ---- pipeline prologue.  Q must be in registers before any later tile load is issued
+  // (the compiler would otherwise wait for it, and so for every load in flight, inside the
+  // loop).  Q is loaded after tile 0 with buffer loads the compiler does not track (rows at
+  // or beyond T load as zeros); with three stages tile 1 follows, so one wait covers tile 0
+  // and Q and tile 1 stays in flight.  The empty asm statements after the wait make Q's
+  // registers defined there.
   // With the ring, tile 0's window (segments 0 .. 2 of both copies and the mirrors of slots
   // 0 and 1: ten loads, three per wave, the surplus repeating) goes first; each later tile's
   // segment is issued one tile ahead, after the barrier that frees its slot.
@@ -432,9 +440,9 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
       }
     }
   }
-  if (ntiles > 1) {
+  if (!RING && ntiles > 1) {
     issue_tile(tB, jb + kNK);
-    BAM_WAIT_VMCNT(RING ? KVL : LPT);   // tile 0 and Q landed (tile 1 may be in flight)
+    BAM_WAIT_VMCNT(LPT);       // tile 0 and Q landed (tile 1 may be in flight)
   } else {
     BAM_WAIT_VMCNT(0);
   }
@@ -449,26 +457,41 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
   BAM_BARRIER_VMCNT(63);       // publish tile 0
   // every wave has waited for its loads of tile t + 1 (in compute_tile); publish it
   auto advance = [&]() { BAM_BARRIER_VMCNT(63); };
-  // tile t's step: issue the ring segment of tile t + 1 (its slot held tile t - 1's first
-  // segment) and the K / V loads of tile t + 2, then compute tile t
-  auto issue_ahead = [&](Tile& tl, int t) {
-    if constexpr (RING) {
-      if (t + 1 < ntiles) ring_next(t + 1);
+  if constexpr (RING) {
+    // Two stages: tile t + 1 and its ring segment (whose slot held tile t - 1's first
+    // segment) load while tile t is computed.  With three waves per SIMD, and the keys of a
+    // short sequence mostly in L2, one tile of lead time is enough; it was 2% faster than
+    // three stages at T = 512 and halves the buffers.
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) {
+        ring_next(t + 1);
+        issue_tile(tB, jb + (t + 1) * kNK);
+      }
+      compute_tile(tA, tB, t);
+      advance();
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) {
+        ring_next(t + 2);
+        issue_tile(tA, jb + (t + 2) * kNK);
+      }
+      compute_tile(tB, tA, t + 1);
+      advance();
     }
-    if (t + 2 < ntiles) issue_tile(tl, jb + (t + 2) * kNK);
-  };
-  for (int t = 0; t < ntiles; t += 3) {
-    issue_ahead(tC, t);
-    compute_tile(tA, tB, t);
-    advance();
-    if (t + 1 >= ntiles) break;
-    issue_ahead(tA, t + 1);
-    compute_tile(tB, tC, t + 1);
-    advance();
-    if (t + 2 >= ntiles) break;
-    issue_ahead(tB, t + 2);
-    compute_tile(tC, tA, t + 2);
-    advance();
+  } else {
+    // Three stages: tile t is computed while tiles t + 1 and t + 2 load.
+    for (int t = 0; t < ntiles; t += 3) {
+      if (t + 2 < ntiles) issue_tile(tC, jb + (t + 2) * kNK);
+      compute_tile(tA, tB, t);
+      advance();
+      if (t + 1 >= ntiles) break;
+      if (t + 3 < ntiles) issue_tile(tA, jb + (t + 3) * kNK);
+      compute_tile(tB, tC, t + 1);
+      advance();
+      if (t + 2 >= ntiles) break;
+      if (t + 4 < ntiles) issue_tile(tB, jb + (t + 4) * kNK);
+      compute_tile(tC, tA, t + 2);
+      advance();
+    }
   }
 
   // ---- epilogue
