@@ -313,10 +313,10 @@ bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void*
 
 // ---------------------------------------------------------------------------------------
 namespace {
-// Backward workspace: the four distance tables (forward layout), D, the per-row scalars of
-// the dK / dV kernel (four arrays over rows padded to 64) and the parameter partials.
+// Backward workspace: the four distance tables (forward layout), the per-row scalars of the
+// dK / dV kernel (four arrays over rows padded to 64) and the parameter partials.
 struct BwdLayout {
-  size_t tab_off, ta_off, tb_off, tm_off, D_off, rs_off, part_off, total;
+  size_t tab_off, ta_off, tb_off, tm_off, rs_off, part_off, total;
   int Tp;
   TableGeom g;
 };
@@ -330,8 +330,7 @@ BwdLayout bwd_layout(int B, int H, int T, bool causal) {
   L.ta_off = tabsz;
   L.tb_off = 2 * tabsz;
   L.tm_off = 3 * tabsz;
-  L.D_off = 4 * tabsz;
-  L.rs_off = L.D_off + align_up((size_t)B * H * T * sizeof(float));
+  L.rs_off = 4 * tabsz;
   L.part_off = L.rs_off + align_up((size_t)4 * B * H * L.Tp * sizeof(float));
   L.total = L.part_off + align_up(bam::bwd_param_partials(B, H, T) * sizeof(float));
   return L;
@@ -406,7 +405,6 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   a.T = T;
   a.causal = causal;
   a.ssmax = (flags & BAM_SSMAX) != 0;
-  a.Dbuf = (float*)(ws + L.D_off);
   a.rowsc = (float*)(ws + L.rs_off);
   a.Tp = L.Tp;
   a.dq_acc = nullptr;

@@ -8,17 +8,18 @@
 // alpha's scale and beta are the trained per-head scalars ("Bayesian Attention
 // Mechanism", "Implementation Details"); the parameter gradients are reduced in fp32.
 //
-// Kernels (all bf16 MFMA 32x32x16, fp32 accumulate, P recomputed from lse):
-//   bwd_pre    D_i = rowsum(dO * O), and the per-row scalars of bwd_dkdv
+// Kernels (all bf16 MFMA 32x32x16, fp32 accumulate, P recomputed from lse), in launch order:
+//   bwd_dq     a work-group owns 128 queries (32 per wave), shaped like the forward
+//              (one query per lane), walks the key tiles: dQ^T += K^T dZ^T, and the
+//              per-element parameter terms are accumulated here, one partial per
+//              work-group (no atomics: the reduction order is fixed).  Each lane first
+//              computes D_i = rowsum(dO * O) of its query and writes the per-row scalars
+//              that bwd_dkdv reads.
 //   bwd_dkdv   a work-group owns 128 keys (32 per wave) and walks the query tiles;
 //              S = Q K^T with queries as MFMA rows and keys as columns puts one key per
 //              lane, so P^T and dZ^T feed dV += P^T dO and dK += dZ^T Q straight from
 //              the accumulators; dO^T and Q^T are transposing LDS reads of the row-major
 //              tiles, which go straight from HBM to LDS, three tiles in flight.
-//   bwd_dq     a work-group owns 128 queries (32 per wave), shaped like the forward
-//              (one query per lane), walks the key tiles: dQ^T += K^T dZ^T, and the
-//              per-element parameter terms are accumulated here, one partial per
-//              work-group (no atomics: the reduction order is fixed).
 //   bwd_params sums the partials of each head (alpha, beta, s and, when wanted, mu).
 // The bias is again the accumulator's initial value (sqrt(Dh) b from the distance
 // window in LDS, -inf where the causal mask forbids the pair); the tables have the
@@ -41,63 +42,6 @@ constexpr int kMQ = 128;     // queries per work-group (dq)
 constexpr int kNK = 64;      // keys per tile (dq)
 
 // ------------------------------------------------------------------------------------
-// D_i = rowsum(dO * O) over rows padded to 64 (bh * Tp + i), and the per-row scalars of
-// the dK / dV kernel: Cl = c log2(e) / sqrt(Dh), L2 = lse log2(e), D, Cq = c / sqrt(Dh);
-// rows at or beyond T get FLT_MIN, +inf, 0, 0 (their weights are exactly zero).
-template <int DH>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a, long nrows_p) {
-  constexpr int LPR = DH / 8;  // lanes per row, 8 elements each
-  const long gt = (long)blockIdx.x * 256 + threadIdx.x;
-  const long rowp = gt / LPR;
-  const int cl = (int)(gt % LPR);
-  const int bh = (int)(rowp / a.Tp);
-  const int i = (int)(rowp - (long)bh * a.Tp);
-  const bool valid = rowp < nrows_p && i < a.T;
-  const long row = (long)bh * a.T + i;
-  float acc = 0.f;
-  if (valid) {
-    const size_t off = (size_t)row * DH + cl * 8;
-    const u32x4 dw = *(const u32x4*)((const uint16_t*)a.dout + off);
-    float ov[8];
-    if (a.o_f32) {
-      const f32x4 o0 = *(const f32x4*)((const float*)a.o + off);
-      const f32x4 o1 = *(const f32x4*)((const float*)a.o + off + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { ov[e] = o0[e]; ov[4 + e] = o1[e]; }
-    } else {
-      const u32x4 ow = *(const u32x4*)((const uint16_t*)a.o + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { ov[2 * e] = bf16_lo(ow[e]); ov[2 * e + 1] = bf16_hi(ow[e]); }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16_lo(dw[e]), ov[2 * e], acc);
-      acc = fmaf(bf16_hi(dw[e]), ov[2 * e + 1], acc);
-    }
-  }
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (rowp < nrows_p && cl == 0) {
-    const size_t n = (size_t)nrows_p;
-    float* rs = a.rowsc + rowp;
-    if (valid) {
-      a.Dbuf[row] = acc;
-      const int h = bh % a.H;
-      const float c = ssmax_c(a.ssmax, a.ssmax ? a.s[h] : 1.0f, a.causal ? i + 1 : a.T);
-      const float isd = 1.0f / __builtin_sqrtf((float)DH);
-      rs[0] = fmaxf(c * kLog2e * isd, FLT_MIN);
-      rs[n] = a.lse[row] * kLog2e;
-      rs[2 * n] = acc;
-      rs[3 * n] = c * isd;
-    } else {
-      rs[0] = FLT_MIN;
-      rs[n] = __builtin_huge_valf();
-      rs[2 * n] = 0.f;
-      rs[3 * n] = 0.f;
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------
 // dK, dV.  A work-group owns kKB = 128 keys (32 per wave; lane ql holds key jw + ql as the
 // MFMA column) and walks the query tiles of 64 rows (causal: from its first key on).
@@ -398,6 +342,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const int i = i0 + wave * 32 + ql;
 
   bf16x8 qf[KS], of[KS];
+  u32x4 dow[KS];   // this lane's dO chunks as loaded (for D)
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 qw = {0u, 0u, 0u, 0u}, ow = {0u, 0u, 0u, 0u};
@@ -407,6 +352,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     }
     qf[ks] = as_bf16x8(qw);
     of[ks] = as_bf16x8(ow);
+    dow[ks] = ow;
   }
   const float sqrtD = __builtin_sqrtf((float)DH);
   const float inv_sqrtD = 1.0f / sqrtD;
@@ -415,7 +361,49 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   const float Cl = fmaxf(c * kLog2e * inv_sqrtD, FLT_MIN);
   const bool valid = i < T;
   const float L2 = valid ? a.lse[(size_t)bh * T + i] * kLog2e : __builtin_huge_valf();
-  const float Di = valid ? a.Dbuf[(size_t)bh * T + i] : 0.f;
+  // D_i = sum_e dO_ie O_ie: this lane's half of the row (the chunks of its Q / dO
+  // operands), then the other half from lane ^ 32
+  // (one loop per O type: a branch inside the loop made the compiler fail)
+  float Dp = 0.f;
+  if (valid && a.o_f32) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t off = base + (size_t)i * DH + 16 * ks + 8 * hh;
+      const f32x4 o0 = *(const f32x4*)((const float*)a.o + off);
+      const f32x4 o1 = *(const f32x4*)((const float*)a.o + off + 4);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        Dp = fmaf(bf16_lo(dow[ks][e]), o0[2 * e], Dp);
+        Dp = fmaf(bf16_hi(dow[ks][e]), o0[2 * e + 1], Dp);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        Dp = fmaf(bf16_lo(dow[ks][2 + e]), o1[2 * e], Dp);
+        Dp = fmaf(bf16_hi(dow[ks][2 + e]), o1[2 * e + 1], Dp);
+      }
+    }
+  } else if (valid) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t off = base + (size_t)i * DH + 16 * ks + 8 * hh;
+      const u32x4 ow = *(const u32x4*)((const uint16_t*)a.o + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Dp = fmaf(bf16_lo(dow[ks][e]), bf16_lo(ow[e]), Dp);
+        Dp = fmaf(bf16_hi(dow[ks][e]), bf16_hi(ow[e]), Dp);
+      }
+    }
+  }
+  const float Di = Dp + xor32(Dp);
+  // the per-row scalars of bwd_dkdv for rows below Tp (rows at or beyond T: zero weight)
+  if (hh == 0 && i < a.Tp) {
+    const size_t n = (size_t)BH * a.Tp;
+    float* rs = a.rowsc + (size_t)bh * a.Tp + i;
+    rs[0] = valid ? Cl : FLT_MIN;
+    rs[n] = L2;
+    rs[2 * n] = valid ? Di : 0.f;
+    rs[3 * n] = valid ? c * inv_sqrtD : 0.f;
+  }
   const float lnn_sd = a.ssmax ? __logf((float)n_i) * inv_sqrtD : 0.f;
 
   f32x16 dq[DB];
@@ -641,24 +629,19 @@ __global__ void __launch_bounds__(64) bwd_params_kernel(BwdArgs a, int nper) {
 
 template <int DH, bool CAUSAL>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-  const long nrows_p = (long)a.B * a.H * a.Tp;
-  const long pre_threads = nrows_p * (DH / 8);
-  hipLaunchKernelGGL(bwd_pre_kernel<DH>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
-                     a, nrows_p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkb = (a.T + kKB - 1) / kKB;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DH, CAUSAL>), dim3((unsigned)(nkb * a.B * a.H)), dim3(256), 0, stream,
-                     a, nkb);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // dQ first: it also writes D and the per-row scalars that the dK / dV kernel reads
   const int nqb = (a.T + kMQ - 1) / kMQ;
-  if (a.tab_dm)
+  if (a.dmu)
     hipLaunchKernelGGL((bwd_dq_kernel<DH, CAUSAL, true>), dim3((unsigned)(nqb * a.B * a.H)), dim3(256), 0,
                        stream, a, nqb);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<DH, CAUSAL, false>), dim3((unsigned)(nqb * a.B * a.H)), dim3(256), 0,
                        stream, a, nqb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (a.T + kKB - 1) / kKB;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DH, CAUSAL>), dim3((unsigned)(nkb * a.B * a.H)), dim3(256), 0, stream,
+                     a, nkb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_params_kernel, dim3(4, a.H), dim3(64), 0, stream, a, a.B * nqb);
