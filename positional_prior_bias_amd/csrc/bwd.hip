@@ -20,7 +20,8 @@
 //              lane, so P^T and dZ^T feed dV += P^T dO and dK += dZ^T Q straight from
 //              the accumulators; dO^T and Q^T are transposing LDS reads of the row-major
 //              tiles, which go straight from HBM to LDS, three tiles in flight.
-//   bwd_params sums the partials of each head (alpha, beta, s and, when wanted, mu).
+//              Its first H work-groups also sum the dQ kernel's partials of each head
+//              (alpha, beta, s and, when wanted, mu).
 // The bias is again the accumulator's initial value (sqrt(Dh) b from the distance
 // window in LDS, -inf where the causal mask forbids the pair); the tables have the
 // forward's layout (reversed, padded, sqrt(Dh) b).
@@ -60,8 +61,24 @@ struct BwdQTile {
   float rs[4][kQT];         // Cl, L2, D, Cq of the tile's rows
 };
 
+// The per-head parameter gradient k (0: alpha, 1: beta, 2: s, 3: mu) of head h: the sum of
+// the dQ kernel's nper partials, by one wave, in float64, in a fixed order.
+__device__ __forceinline__ void reduce_param(const BwdArgs& a, int h, int k, int nper, int lane) {
+  if (k == 3 && a.dmu == nullptr) return;
+  double acc = 0.0;
+  for (int x = lane; x < nper; x += 64) acc += (double)a.param_part[((size_t)h * nper + x) * 4 + k];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) {
+    float* out = k == 0 ? a.dalpha : (k == 1 ? a.dbeta : (k == 2 ? a.ds : a.dmu));
+    out[h] = (k == 2 && !a.ssmax) ? 0.f : (float)acc;
+  }
+}
+
+// The first H work-groups also reduce the parameter gradients of head blockIdx.x (the dQ
+// kernel, which wrote the partials, has finished: same stream).
 template <int DH, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb, int nper) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
   constexpr int KCH = DH / 8;                 // 16-byte chunks per row
@@ -86,6 +103,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31;
   const int hh = lane >> 5;
+  if ((int)blockIdx.x < a.H) reduce_param(a, blockIdx.x, wave, nper, lane);
   const int j0 = kb * kKB;
   const int jw = j0 + 32 * wave;
   const int j = jw + ql;   // this lane's key
@@ -612,21 +630,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   }
 }
 
-// ------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(64) bwd_params_kernel(BwdArgs a, int nper) {
-  const int k = blockIdx.x;   // 0: alpha, 1: beta, 2: s, 3: mu
-  const int h = blockIdx.y;
-  double acc = 0.0;
-  if (k == 3 && a.dmu == nullptr) return;
-  for (int x = threadIdx.x; x < nper; x += 64) acc += (double)a.param_part[((size_t)h * nper + x) * 4 + k];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (threadIdx.x == 0) {
-    float* out = k == 0 ? a.dalpha : (k == 1 ? a.dbeta : (k == 2 ? a.ds : a.dmu));
-    out[h] = (k == 2 && !a.ssmax) ? 0.f : (float)acc;
-  }
-}
-
 template <int DH, bool CAUSAL>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   // dQ first: it also writes D and the per-row scalars that the dK / dV kernel reads
@@ -641,10 +644,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int nkb = (a.T + kKB - 1) / kKB;
   hipLaunchKernelGGL((bwd_dkdv_kernel<DH, CAUSAL>), dim3((unsigned)(nkb * a.B * a.H)), dim3(256), 0, stream,
-                     a, nkb);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_params_kernel, dim3(4, a.H), dim3(64), 0, stream, a, a.B * nqb);
+                     a, nkb, a.B * nqb);
   return hipGetLastError();
 }
 
