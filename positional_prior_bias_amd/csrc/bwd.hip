@@ -19,7 +19,7 @@
 //              S = Q K^T with queries as MFMA rows and keys as columns puts one key per
 //              lane, so P^T and dZ^T feed dV += P^T dO and dK += dZ^T Q straight from
 //              the accumulators; dO^T and Q^T are transposing LDS reads of the row-major
-//              tiles, which go straight from HBM to LDS, three tiles in flight.
+//              tiles, which go straight from HBM to LDS, one tile ahead.
 //              Its first H work-groups also sum the dQ kernel's partials of each head
 //              (alpha, beta, s and, when wanted, mu).
 // The bias is again the accumulator's initial value (sqrt(Dh) b from the distance
@@ -51,8 +51,8 @@ constexpr int kNK = 64;      // keys per tile (dq)
 // contraction runs over the queries in the order the accumulator holds them); the B
 // operands dO^T and Q^T are transposing reads of the row-major tiles.
 // A query tile (Q, dO, the distance window and the four per-row scalars) goes straight from
-// HBM to LDS with buffer loads issued from inline assembly; three tiles in flight, one
-// barrier per tile.  Rows at or beyond T load as zeros and carry zero weight.
+// HBM to LDS with buffer loads issued from inline assembly, one tile ahead, one barrier per
+// tile.  Rows at or beyond T load as zeros and carry zero weight.
 template <int DH>
 struct BwdQTile {
   uint16_t q[kQT * DH];     // swizzled 16-byte chunks, as the forward's K / V tiles
@@ -78,14 +78,16 @@ __device__ __forceinline__ void reduce_param(const BwdArgs& a, int h, int k, int
 // The first H work-groups also reduce the parameter gradients of head blockIdx.x (the dQ
 // kernel, which wrote the partials, has finished: same stream).
 template <int DH, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb, int nper) {
+__global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, int nper) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
   constexpr int KCH = DH / 8;                 // 16-byte chunks per row
   constexpr int CPW = kQT * KCH / 256;        // direct 16-byte loads per wave per tensor
-  constexpr int LPT = 2 * CPW + 2;            // direct loads per wave per tile
   static_assert(kQT * KCH % 256 == 0 && (kQT + kKB) == 3 * 64, "tile shape");
-  __shared__ __attribute__((aligned(16))) BwdQTile<DH> tA, tB, tC;
+  // Two buffers (36 KB at Dh = 64) and at most 168 VGPRs: three work-groups, three waves per
+  // SIMD, fit a CU.  The third wave hides the MFMA -> exp -> MFMA chain that two waves left
+  // exposed; 14% faster than three pipeline stages at two waves per SIMD.
+  __shared__ __attribute__((aligned(16))) BwdQTile<DH> tA, tB;
 
   const int BH = a.B * a.H;
   const int kb = blockIdx.x / BH;
@@ -258,36 +260,21 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb, in
     }
   };
 
-  // three-stage pipeline: tile t is computed while tiles t + 1 and t + 2 load; each wave
-  // waits for its own loads of tile t + 1, then the barrier publishes it
-  auto wait_next = [&](int t) __attribute__((always_inline)) {
-    if (t + 1 >= ntiles) return;
-    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
-    else BAM_WAIT_VMCNT(0);
-  };
+  // two-stage pipeline: tile t + 1 loads while tile t is computed; each wave waits for its
+  // own loads, then the barrier publishes the tile
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, qstart);
-  if (ntiles > 1) {
-    issue_tile(tB, qstart + kQT);
-    BAM_WAIT_VMCNT(LPT);
-  } else {
-    BAM_WAIT_VMCNT(0);
-  }
+  BAM_WAIT_VMCNT(0);
   BAM_BARRIER_VMCNT(63);       // publish tile 0
-  for (int t = 0; t < ntiles; t += 3) {
-    if (t + 2 < ntiles) issue_tile(tC, qstart + (t + 2) * kQT);
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) issue_tile(tB, qstart + (t + 1) * kQT);
     compute(tA, qstart + t * kQT);
-    wait_next(t);
+    BAM_WAIT_VMCNT(0);
     BAM_BARRIER_VMCNT(63);
     if (t + 1 >= ntiles) break;
-    if (t + 3 < ntiles) issue_tile(tA, qstart + (t + 3) * kQT);
+    if (t + 2 < ntiles) issue_tile(tA, qstart + (t + 2) * kQT);
     compute(tB, qstart + (t + 1) * kQT);
-    wait_next(t + 1);
-    BAM_BARRIER_VMCNT(63);
-    if (t + 2 >= ntiles) break;
-    if (t + 4 < ntiles) issue_tile(tB, qstart + (t + 4) * kQT);
-    compute(tC, qstart + (t + 2) * kQT);
-    wait_next(t + 2);
+    BAM_WAIT_VMCNT(0);
     BAM_BARRIER_VMCNT(63);
   }
 
@@ -316,7 +303,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a, int nkb, in
 // tiles of 64.  S^T = K Q^T and dP^T = V dO^T put the keys on the MFMA rows, so dZ^T leaves
 // the accumulators in the B-operand layout of dQ^T += K^T dZ^T; K^T is a transposing read of
 // the row-major K tile.  A key tile (K, V and the windows of the bias and derivative tables)
-// goes straight from HBM to LDS, three tiles in flight, one barrier per tile.
+// goes straight from HBM to LDS, one tile ahead, one barrier per tile.
 // MU: also accumulate the offset term c dZ db/dmu (db/dmu table tab_dm).
 template <int DH>
 struct BwdKTile {
@@ -326,7 +313,7 @@ struct BwdKTile {
 };
 
 template <int DH, bool CAUSAL, bool MU>
-__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
+__global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   constexpr int KS = DH / 16;
   constexpr int DB = DH / 32;
   constexpr int KCH = DH / 8;
@@ -334,9 +321,11 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
   constexpr int NTAB = MU ? 4 : 3;            // tables whose windows are loaded
   constexpr int NWL = 3 * NTAB;               // 64-entry window loads per tile (all waves)
   constexpr int WPW = (NWL + 3) / 4;          // per wave; surplus slots repeat the last load
-  constexpr int LPT = 2 * CPW + WPW;          // direct loads per wave per tile
   static_assert(kNK * KCH % 256 == 0 && kMQ + kNK == 3 * 64, "tile shape");
-  __shared__ __attribute__((aligned(16))) BwdKTile<DH> tA, tB, tC;
+  // Two buffers (39 KB at Dh = 64) and at most 168 VGPRs: three waves per SIMD (Dh = 64;
+  // at Dh = 32 the offset-gradient variant would spill, so it keeps two); 11% faster than
+  // three pipeline stages at two waves per SIMD.
+  __shared__ __attribute__((aligned(16))) BwdKTile<DH> tA, tB;
   __shared__ float red[4][4];
 
   const int BH = a.B * a.H;
@@ -558,35 +547,20 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a, int nqb) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // three-stage pipeline, as the dK / dV kernel
-  auto wait_next = [&](int t) __attribute__((always_inline)) {
-    if (t + 1 >= ntiles) return;
-    if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);
-    else BAM_WAIT_VMCNT(0);
-  };
+  // two-stage pipeline, as the dK / dV kernel
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, 0);
-  if (ntiles > 1) {
-    issue_tile(tB, kNK);
-    BAM_WAIT_VMCNT(LPT);
-  } else {
-    BAM_WAIT_VMCNT(0);
-  }
+  BAM_WAIT_VMCNT(0);
   BAM_BARRIER_VMCNT(63);       // publish tile 0
-  for (int t = 0; t < ntiles; t += 3) {
-    if (t + 2 < ntiles) issue_tile(tC, (t + 2) * kNK);
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) issue_tile(tB, (t + 1) * kNK);
     compute(tA, t * kNK);
-    wait_next(t);
+    BAM_WAIT_VMCNT(0);
     BAM_BARRIER_VMCNT(63);
     if (t + 1 >= ntiles) break;
-    if (t + 3 < ntiles) issue_tile(tA, (t + 3) * kNK);
+    if (t + 2 < ntiles) issue_tile(tA, (t + 2) * kNK);
     compute(tB, (t + 1) * kNK);
-    wait_next(t + 1);
-    BAM_BARRIER_VMCNT(63);
-    if (t + 2 >= ntiles) break;
-    if (t + 4 < ntiles) issue_tile(tB, (t + 4) * kNK);
-    compute(tC, (t + 2) * kNK);
-    wait_next(t + 2);
+    BAM_WAIT_VMCNT(0);
     BAM_BARRIER_VMCNT(63);
   }
 
