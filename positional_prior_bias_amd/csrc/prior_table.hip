@@ -79,6 +79,7 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   const double a = alpha[h];
   const double be = beta[h];
   const double m = mu ? (double)mu[h] : 0.0;
+  const bool der = ta || tb || tm;   // derivative tables wanted (the forward's table is bias only)
   double b, da = 0.0, db = 0.0, dm = 0.0;
   if (kind == kPriorSandwich) {
     if (nf > kSandwichMaxFreq) {
@@ -96,10 +97,12 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
     const double g = fabs(x) + (double)BAM_REF_EPS;
     double l2g;
     b = -exp(a) * pow_pos(g, be, l2g);
-    da = b;
-    db = b * l2g * 0.6931471805599453;   // b ln g
-    const double sg = x > 0.0 ? 1.0 : (x < 0.0 ? -1.0 : 0.0);
-    dm = -b * be * sg / g * (em + emi);
+    if (der) {
+      da = b;
+      db = b * l2g * 0.6931471805599453;   // b ln g
+      const double sg = x > 0.0 ? 1.0 : (x < 0.0 ? -1.0 : 0.0);
+      dm = -b * be * sg / g * (em + emi);
+    }
   } else {
     const double x = (double)d - m;
     const double u = __builtin_isinf(a) ? 0.0 : fabs(x) / a;
@@ -112,9 +115,11 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
       double l2u;
       const double p = pow_pos(u, be, l2u);
       b = -p;
-      da = be * p / a;
-      db = -p * l2u * 0.6931471805599453;  // -p ln u
-      dm = be * p / x;                             // db/dmu, dx/dmu = -1
+      if (der) {
+        da = be * p / a;
+        db = -p * l2u * 0.6931471805599453;  // -p ln u
+        dm = be * p / x;                     // db/dmu, dx/dmu = -1
+      }
     }
   }
   tab[idx] = (float)(b * scale);
