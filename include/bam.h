@@ -235,8 +235,8 @@ bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void*
  * 16 * B * H * (T rounded up to 64) <= 2^31 - 1 (the kernels address one head's Q / dO and
  * the per-row scalars with 32-bit byte ranges); BAM_EUNSUPPORTED otherwise.
  * Workspace (bam_bwd_workspace_size): the bias and derivative tables over the padded
- * distance range, D and four per-row scalars over rows padded to 64, and the per-head
- * partial sums; contents are scratch between calls.
+ * distance range, four per-row fp32 scalars (D_i among them) over rows padded to 64, and
+ * the per-head partial sums; contents are scratch between calls.
  */
 size_t bam_bwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
 bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
