@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -49,8 +50,13 @@ def fwd_flops(B, H, T, Dh, causal=True):
 
 
 def src_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of a kernel source's code: comments and blank lines are dropped first, so
+    an edit to comments alone leaves the committed counter summary valid."""
+    with open(path, encoding="utf-8") as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    lines = (re.sub(r"//.*", "", l).rstrip() for l in text.splitlines())
+    code = "\n".join(l for l in lines if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 class Timer:

@@ -72,12 +72,14 @@ struct FwdTile<DH, 0> {
 
 // The ring: segment k of local tile t sits in slot (t + k) & 3 (64 entries each), and slots 0
 // and 1 are mirrored after slot 3, so tile t's window is the 192 contiguous entries from
-// 64 (t & 3).  Per copy 384 entries, copies kRingStride floats apart (400 = 12 * 32 + 16).
-// It keeps a work-group of 128 rows (Dh = 64) at 52,288 bytes of LDS: three fit in a CU's
-// 160 KiB, which the hardware allocates in steps of 1,280 bytes (three per-buffer windows
-// would need 54,144 bytes, and only two would fit).
+// 64 (t & 3).  Per copy 384 entries, copies kRingStride floats apart (400 = 12 * 32 + 16, so
+// the two copies start on different banks).  The ring takes 3,200 bytes of LDS for the whole
+// pipeline instead of a window per tile buffer; with two 16 KiB K / V buffers a work-group of
+// 128 rows (Dh = 64) needs 35,968 bytes, and its 141 VGPRs, not LDS, hold a CU to three
+// work-groups.  (The CU allocates LDS in steps of 1,280 bytes.)
 constexpr int kRingEntries = 384;
 constexpr int kRingStride = 400;
+static_assert(kRingStride >= kRingEntries && kRingStride % 32 == 16, "ring copies overlap or share banks");
 
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
