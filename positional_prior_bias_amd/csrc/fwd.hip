@@ -75,8 +75,8 @@ struct FwdTile<DH, 0> {
 // 64 (t & 3).  Per copy 384 entries, copies kRingStride floats apart (400 = 12 * 32 + 16, so
 // the two copies start on different banks).  The ring takes 3,200 bytes of LDS for the whole
 // pipeline instead of a window per tile buffer; with two 16 KiB K / V buffers a work-group of
-// 128 rows (Dh = 64) needs 35,968 bytes, and its 141 VGPRs, not LDS, hold a CU to three
-// work-groups.  (The CU allocates LDS in steps of 1,280 bytes.)
+// 128 rows (Dh = 64) needs 35,968 bytes (37,120 in the CU's 1,280-byte allocation steps), so
+// four fit in a CU's 160 KiB, and its 126 VGPRs allow four waves per SIMD.
 constexpr int kRingEntries = 384;
 constexpr int kRingStride = 400;
 static_assert(kRingStride >= kRingEntries && kRingStride % 32 == 16, "ring copies overlap or share banks");
@@ -84,7 +84,7 @@ static_assert(kRingStride >= kRingEntries && kRingStride % 32 == 16, "ring copie
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
 template <int DH, bool CAUSAL, int NQB>
-__global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
+__global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
   constexpr int QW = 32 * NQB;          // query rows per wave
   constexpr int MQ = 4 * QW;            // query rows per work-group
   constexpr int TW = MQ + kNK;          // distance-window entries per tile (multiple of 64)
@@ -379,8 +379,11 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
       l[qb2] += ls[0] + ls[1];
     }
 
-    // the next tile's V is converted here, between the softmax and the PV product
-    convert_next(nx, t);
+    // The next tile's V is converted between the softmax and the PV product in the 256-row
+    // kernel, and after the PV product in the 128-row one.  There the later wait gives the
+    // loads a whole tile of lead time and the shorter live ranges cut the VGPRs from 141 to
+    // 126 (T = 512 and 1,024: 2-3% faster; the 256-row kernel was 6-10% slower that way).
+    if constexpr (NQB != 1) convert_next(nx, t);
 
     // ---- O^T += V^T P^T (fp16).  The V^T operand of lane (dh, hh) holds keys
     // {16 st + 4 hh + 0..3, + 8 .. + 11} of column dh: two transposing reads of the
@@ -416,6 +419,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 3 : 2) fwd_bf16_
           oacc[qb2][db] = mfma32x32x16_f16(av[st], as_f16x8(pf[qb2][st]), oacc[qb2][db]);
       if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
     }
+    if constexpr (NQB == 1) convert_next(nx, t);
   };
 
   // ---- pipeline prologue.  Q must be in registers before any later tile load is issued
