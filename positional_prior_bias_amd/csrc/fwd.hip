@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   constexpr int CPW = kNK * KCH / 256;  // 1 KiB direct loads per wave per tensor
   // Copies of the window: 4 (each lane's runs of 4 distances are one 16-byte read); 2 for
   // Dh = 64 with one query block per wave (8-byte reads), which keeps the work-group's LDS
-  // under a third of the CU's so three work-groups (three waves per SIMD) fit.
+  // under a quarter of the CU's so four work-groups (four waves per SIMD) fit.
   constexpr int NCOPY = (DH == 64 && NQB == 1) ? 2 : 4;
   constexpr bool RING = NCOPY == 2;               // two copies: the window is the shared ring
   static_assert(!RING || TW == 192, "the ring holds windows of three 64-entry segments");
@@ -473,7 +473,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   auto advance = [&]() { BAM_BARRIER_VMCNT(63); };
   if constexpr (RING) {
     // Two stages: tile t + 1 and its ring segment (whose slot held tile t - 1's first
-    // segment) load while tile t is computed.  With three waves per SIMD, and the keys of a
+    // segment) load while tile t is computed.  With three or more waves per SIMD, and the keys of a
     // short sequence mostly in L2, one tile of lead time is enough; it was 2% faster than
     // three stages at T = 512 and halves the buffers.
     for (int t = 0; t < ntiles; t += 2) {
