@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   const int BH = a.B * a.H;
   // Work-group i runs on XCD i % 8 (one L2 each).  With B * H a multiple of 8 every query
   // block of a head lands on that head's XCD, so the blocks of a head running together
-  // share its K / V tiles in one L2 (36% fewer HBM fetches than spreading them at T = 512).
+  // share its K / V tiles in one L2 (spread over four XCDs, they fetched 36% more at T = 512).
   const int bid = blockIdx.x;
   int qb = bid / BH;
   const int bh = bid - qb * BH;
