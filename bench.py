@@ -37,6 +37,7 @@ METRIC = "BAM attn fwd TFLOP/s @T=512 & 32k (% MFMA peak); decode GB/s @256k KV"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COUNTERS = os.path.join(ROOT, "profiles", "fwd_bf16_kernel_T512_counters.json")
+SPIN_CYCLES = 20_000_000    # about 8 ms of GPU clock: time for the host to queue the timed launches
 FWD_SRC = os.path.join(ROOT, "positional_prior_bias_amd", "csrc", "fwd.hip")
 
 
@@ -101,11 +102,15 @@ class Timer:
 
     def per_launch(self, fn, launches, warmup=2):
         """Average duration of one launch of `fn`'s kernel: one event pair around `launches`
-        back-to-back launches on the stream the kernel runs on."""
+        back-to-back launches on the stream the kernel runs on.  A bounded spin kernel
+        (torch.cuda._sleep) runs first on that stream, so the host has queued every launch
+        before the GPU reaches the first event: the pair then measures GPU time even where
+        one Python call takes longer than one kernel."""
         torch = self.torch
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()

@@ -550,6 +550,9 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a, int nqb) {
   __shared__ __attribute__((aligned(16))) float Ks[kNK32 * DH];
   __shared__ __attribute__((aligned(16))) float Vs[kNK32 * DH];
   __shared__ float tw[kMQ32 + kNK32];
+  // the lane's scores of one key tile, column `lane` (a register array indexed in a
+  // partially unrolled loop would live in scratch memory)
+  __shared__ float scs[kNK32 * kMQ32];
 
   const int BH = a.B * a.H;
   int qb = blockIdx.x / BH;
@@ -605,7 +608,6 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a, int nqb) {
     }
     __syncthreads();
     const int nk = min(kNK32, kend - j0);
-    float sc[kNK32];
     float mx = kNegInf;
 #pragma unroll 4
     for (int jj = 0; jj < kNK32; ++jj) {
@@ -615,7 +617,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a, int nqb) {
       const float bv = tw[lane + (kNK32 - 1) - jj];
       float t = fmaf(Cs, dot, Cb * bv);
       if (jj >= nk || bv == kNegInf) t = kNegInf;
-      sc[jj] = t;
+      scs[jj * kMQ32 + lane] = t;
       mx = fmaxf(mx, t);
     }
     const float m_new = fmaxf(m, mx);
@@ -627,7 +629,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a, int nqb) {
     for (int e = 0; e < DH; ++e) o[e] *= s0;
 #pragma unroll 2
     for (int jj = 0; jj < kNK32; ++jj) {
-      const float p = exp2_fast(sc[jj] - m_use);
+      const float p = exp2_fast(scs[jj * kMQ32 + lane] - m_use);
       l += p;
 #pragma unroll
       for (int e = 0; e < DH; ++e) o[e] = fmaf(p, Vs[jj * DH + e], o[e]);
