@@ -110,7 +110,9 @@ class Timer:
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        torch.cuda._sleep(SPIN_CYCLES)
+        spin = getattr(torch.cuda, "_sleep", None)   # private torch API: without it the pair
+        if spin is not None:                           # may include host launch time
+            spin(SPIN_CYCLES)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
