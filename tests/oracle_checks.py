@@ -502,6 +502,60 @@ def check_sandwich_special_cases(orc):
     _close(orc.prior_bias_sandwich(np.array([1]), 1.0, 128.0), [np.sum(np.cos(w))], 1e-12, "sandwich at d = 1")
 
 
+def check_conditioning_scales_brute(orc):
+    """The conditioning scales A_theta of the parameter-gradient sums (sum over the visible
+    pairs of |term|), recomputed with explicit scalar loops on T <= 6: softmax without max
+    subtraction, the backward's terms written out per pair from the chain rule, and the
+    derivatives of b = -(|d - mu| / alpha)^beta in closed form.  Also A_theta >= |dtheta|
+    (triangle inequality) and the sums themselves."""
+    rng = np.random.default_rng(11)
+    for causal, ssmax, T in ((True, True, 6), (False, True, 5), (True, False, 4)):
+        B, H, Dh = 1, 2, 3
+        q = rng.standard_normal((B, H, T, Dh))
+        k = rng.standard_normal((B, H, T, Dh))
+        v = rng.standard_normal((B, H, T, Dh))
+        do = rng.standard_normal((B, H, T, Dh))
+        alpha = np.array([1.7, 3.1])
+        beta = np.array([0.6, 1.4])
+        mu = np.array([0.35, -0.5])
+        s = np.array([0.45, 0.8])
+        got = orc.attn_bwd(q, k, v, do, alpha, beta, mu, s, causal=causal, ssmax=ssmax)
+        for h in range(H):
+            sums = [0.0, 0.0, 0.0, 0.0]    # dalpha, dbeta, dmu, ds
+            scales = [0.0, 0.0, 0.0, 0.0]
+            for i in range(T):
+                keys = [j for j in range(T) if (j <= i or not causal)]
+                n = len(keys)
+                c = s[h] * math.log(n) if ssmax else 1.0
+                S = {j: sum(q[0, h, i, e] * k[0, h, j, e] for e in range(Dh)) / math.sqrt(Dh) for j in keys}
+                u = {j: abs((i - j) - mu[h]) / alpha[h] for j in keys}
+                bias = {j: -(u[j] ** beta[h]) for j in keys}
+                ex = {j: math.exp(c * (S[j] + bias[j])) for j in keys}
+                Z = sum(ex.values())
+                P = {j: ex[j] / Z for j in keys}
+                O = [sum(P[j] * v[0, h, j, e] for j in keys) for e in range(Dh)]
+                dP = {j: sum(do[0, h, i, e] * v[0, h, j, e] for e in range(Dh)) for j in keys}
+                D = sum(do[0, h, i, e] * O[e] for e in range(Dh))
+                for j in keys:
+                    dZ = P[j] * (dP[j] - D)
+                    uu, x = u[j], (i - j) - mu[h]
+                    db_da = beta[h] * uu ** beta[h] / alpha[h] if uu > 0 else 0.0
+                    db_db = -(uu ** beta[h]) * math.log(uu) if uu > 0 else 0.0
+                    db_dm = beta[h] * uu ** beta[h] / x if uu > 0 else 0.0
+                    terms = [c * dZ * db_da, c * dZ * db_db, c * dZ * db_dm,
+                             dZ * math.log(n) * (S[j] + bias[j]) if ssmax else 0.0]
+                    for t_ in range(4):
+                        sums[t_] += terms[t_]
+                        scales[t_] += abs(terms[t_])
+            for t_, (gname, aname) in enumerate((("dalpha", "A_alpha"), ("dbeta", "A_beta"), ("dmu", "A_mu"),
+                                                 ("ds", "A_s"))):
+                _close([got[aname][h]], [scales[t_]], 1e-12 * max(1.0, scales[t_]),
+                       f"{aname} brute force causal={causal} ssmax={ssmax} head {h}")
+                _close([got[gname][h]], [sums[t_]], 1e-12 * max(1.0, scales[t_]),
+                       f"{gname} brute force causal={causal} ssmax={ssmax} head {h}")
+                assert got[aname][h] >= abs(got[gname][h]) * (1 - 1e-12), f"{aname} < |{gname}|"
+
+
 ALL_CHECKS = [
     check_worked_example, check_closed_form_offset_ssmax, check_closed_form_content,
     check_alibi_reduction, check_nope_reduction, check_gaussian_reduction, check_sqrt_reductions,
@@ -509,4 +563,5 @@ ALL_CHECKS = [
     check_dalpha_alibi_closed_form, check_special_values,
     check_ref_mu_is_two_sinh, check_ref_reduces_to_alpha_form, check_ref_special_values,
     check_param_derivatives_fd, check_backward_fd_ref, check_sandwich_special_cases,
+    check_conditioning_scales_brute,
 ]

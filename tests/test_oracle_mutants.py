@@ -47,6 +47,10 @@ MUTANTS = {
                                              "np.cos(d / 10000.0 ** (1.0 * i / float(d_bar)))"),
     "sandwich: ratio multiplies": ("return out / float(ratio)", "return out * float(ratio)"),
     "sandwich: one frequency too many": ("nf = int(float(d_bar)) // 2", "nf = int(float(d_bar)) // 2 + 1"),
+    "A_alpha without |.|": ("A[0, h] += np.abs(ta).sum()", "A[0, h] += ta.sum()"),
+    "A_beta from the alpha terms": ("A[1, h] += np.abs(tb).sum()", "A[1, h] += np.abs(ta).sum()"),
+    "A_s without ln n": ("A[2, h] += np.abs(tsum).sum()", "A[2, h] += np.abs(tsum / lnn).sum()"),
+    "A_mu over every entry": ("A[3, h] += np.abs(tm).sum()", "A[3, h] += np.abs(tm).sum() + np.abs(c * dZ).sum()"),
     "dmu sign": ("out[nz] = beta * np.power(u[nz], beta) / x[nz]", "out[nz] = -beta * np.power(u[nz], beta) / x[nz]"),
 }
 
