@@ -154,6 +154,10 @@ bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float
  * Without BAM_CAUSAL every query sees all T keys (n_i = T).
  * o: [B, H, T, Dh] of o_dtype (BAM_BF16 output is the round-to-nearest-even of the
  * float32 result).  lse: [B, H, T] float32, natural log.
+ * Precision of the bf16 path: Q K^T and P V run on bf16 MFMA with fp32 accumulation; the
+ * softmax weights are rounded to bf16 for P V, each at most 1 (the running row maximum is
+ * exact), while the row sum and lse use the unrounded fp32 weights.  Any finite bf16 V
+ * is accepted.
  * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128} (bf16 MFMA, fp32 accumulate) and
  * T * Dh * 2 < 2^31 bytes per (b, h); in_dtype BAM_F32 with Dh in {32, 64} (fp32
  * throughout).  Larger requests return BAM_EUNSUPPORTED.  BAM_SKIP_FAR: see above.

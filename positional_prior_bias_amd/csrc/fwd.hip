@@ -23,15 +23,13 @@
 //     (stored in reverse distance order, so a lane's values are read in register order),
 //     and the MFMA returns q.k + sqrt(Dh) b directly.  Distances the causal mask forbids
 //     hold -inf in that window, so masking is free as well.
-//   * The running max moves lazily: the reference max of a row changes only when a tile's
-//     max exceeds it by more than 2^8 (O and l are multiplied by the factor every tile, by
-//     1 when the reference holds; this keeps the tile one basic block).
-//   * O^T = V^T P^T with P and V in fp16 (v_mfma_f32_32x32x16_f16): P^T is fed from the
-//     S^T accumulators without any lane exchange (the contraction index runs over the keys
-//     in the order the accumulator holds them); V^T comes from transposing LDS reads of the
-//     row-major tile, which each wave converts from bf16 to fp16 for the chunks it loaded.
-//     l sums the same fp16-rounded weights, so O / l is a convex combination of V rows and
-//     lse is within 2^-11 of the fp32 value.
+//   * The running max of a row is exact, so every weight is at most 1 when it is rounded to
+//     bf16 for the PV product (O and l are multiplied by the rescale factor every tile, by
+//     1 when the max holds; this keeps the tile one basic block).
+//   * O^T = V^T P^T on bf16 MFMA: P^T is fed from the S^T accumulators (rounded to bf16)
+//     without any lane exchange (the contraction index runs over the keys in the order the
+//     accumulator holds them); V^T comes from transposing LDS reads of the row-major tile.
+//     l sums the unrounded fp32 weights, so lse carries fp32 rounding only.
 //   * K / V rows in LDS have their 16-byte chunks XOR-swizzled by row so operand reads do
 //     not collide in banks.
 //   * With a skipping plan (causal only), a work-group starts its key loop at the first
@@ -102,7 +100,6 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   static_assert(RING || NCOPY * (TW / 64) % 4 == 0, "window loads split over four waves");
   constexpr int KVL = 2 * CPW;          // K / V direct loads per wave per tile
   constexpr int LPT = KVL + WPW;        // direct-load instructions per wave per tile
-  constexpr float kLazy = 8.0f;         // rescale only when a row max grows by > 2^8
   // Two 32-row blocks per wave: each block of MFMAs is issued at raised wave priority, so
   // a wave with matrix work ready goes ahead of the other wave's softmax (about 4% at
   // T = 32768; neutral for one block per wave, where it is left out).
@@ -185,19 +182,26 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   const i32x4 rK = buffer_rsrc(K, (uint32_t)T * DH * 2);
   const i32x4 rV = buffer_rsrc(V, (uint32_t)T * DH * 2);
   const i32x4 rW = buffer_rsrc(tabh, (uint32_t)a.tab_stride * 4);
-  int kv_voff[CPW];
-#pragma unroll
-  for (int r = 0; r < CPW; ++r) {
-    const int p = (wave * CPW + r) * 64 + lane;
+  // Per-lane byte offset of direct load r.  In the 128-row kernel the offsets are recomputed
+  // at each issue from a lane id the compiler cannot see through: kept live across the tile
+  // they pushed it past its 128 VGPRs, and the spill reloads waited for every load in flight.
+  auto issue_lane = [&]() {
+    int ln = lane;
+    if constexpr (NQB == 1) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
+  };
+  auto kv_voff = [&](int r) {
+    const int p = (wave * CPW + r) * 64 + issue_lane();
     const int row = p / KCH;
-    kv_voff[r] = (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
-  }
+    return (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
+  };
   auto issue_tile = [&](Tile& tl, int j0) {
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       const int p0 = (wave * CPW + r) * 64;
-      lds_dma16(rK, kv_voff[r] + j0 * DH * 2, 0, &tl.k[p0 * 8]);
-      lds_dma16(rV, kv_voff[r] + j0 * DH * 2, 0, &tl.v[p0 * 8]);
+      const int vo = kv_voff(r) + j0 * DH * 2;
+      lds_dma16(rK, vo, 0, &tl.k[p0 * 8]);
+      lds_dma16(rV, vo, 0, &tl.v[p0 * 8]);
     }
     if constexpr (!RING) {
       const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
@@ -217,7 +221,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     const int u0 = a.tab_d0 - (i0 + MQ - 1 - (jb + t * kNK));
     const int slot = (t + k) & 3;
     const int pos = (mirror && slot < 2) ? 256 + 64 * slot : 64 * slot;
-    lds_dma4(rW, lane * 4, (u0 + cpy + 64 * k) * 4, &wring[cpy * kRingStride + pos]);
+    lds_dma4(rW, issue_lane() * 4, (u0 + cpy + 64 * k) * 4, &wring[cpy * kRingStride + pos]);
   };
   // the segment tile t adds (k = 2): one load per wave (copy wave & 1, mirror wave >> 1)
   auto ring_next = [&](int t) { ring_load(t, 2, wave & 1, wave >> 1); };
@@ -238,21 +242,9 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     for (int ks = 0; ks < KS; ++ks) kOff[ks] = 128 * ql + 16 * ((2 * ks + hh) ^ vswz<DH>(ql));
   }
 
-  // ---- V is converted from bf16 to fp16 in LDS once per tile, each wave converting the
-  // chunks its own direct loads wrote (so it only waits for its own loads), before the
-  // barrier that publishes the tile.  P is rounded to fp16 for the PV product.
-  auto convert_v = [&](Tile& tl) {
-#pragma unroll
-    for (int r = 0; r < CPW; ++r) {
-      u32x4* pv = (u32x4*)&tl.v[((wave * CPW + r) * 64 + lane) * 8];
-      const u32x4 w = *pv;
-      const u32x4 hw = {bf16x2_to_f16x2(w[0]), bf16x2_to_f16x2(w[1]), bf16x2_to_f16x2(w[2]),
-                        bf16x2_to_f16x2(w[3])};
-      *pv = hw;
-    }
-  };
-  // wait for this wave's loads of tile t + 1 (tile t + 2's may stay in flight), convert it
-  auto convert_next = [&](Tile& nx, int t) {
+  // Before the barrier that publishes tile t + 1, each wave waits for its own loads of it
+  // (tile t + 2's may stay in flight).
+  auto wait_next = [&](int t) {
     if (t + 1 >= ntiles) return;
     if constexpr (RING) {
       BAM_WAIT_VMCNT(0);          // two stages: only tile t + 1's loads are in flight
@@ -260,17 +252,16 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       if (t + 2 < ntiles) BAM_WAIT_VMCNT(LPT);   // tile t + 2's stay in flight
       else BAM_WAIT_VMCNT(0);
     }
-    convert_v(nx);
   };
 
-  auto compute_tile = [&](const Tile& tl, Tile& nx, int t) {
+  auto compute_tile = [&](const Tile& tl, int t) {
     const int j0 = jb + t * kNK;
     // A wave whose rows all precede this tile's keys has nothing to do (causal).  Without
     // the mask the second test never holds (tiles end before T), but the branch splits the
     // tile into its own scheduling region: as one region with the loop around it, the
     // compiler's schedule needs more than the 256 registers of two waves per SIMD.
     if ((CAUSAL && j0 > iw + QW - 1) || (!CAUSAL && j0 >= T)) {
-      convert_next(nx, t);
+      wait_next(t);
       return;
     }
     // ---- S'^T = K Q^T + sqrt(Dh) b: each accumulator starts from its bias block (read
@@ -338,7 +329,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
           }
     }
 
-    // ---- online softmax (exp2 domain) with lazy rescaling
+    // ---- online softmax (exp2 domain) with an exact running max
     u32x4 pf[NQB][4];
 #pragma unroll
     for (int qb2 = 0; qb2 < NQB; ++qb2) {
@@ -351,12 +342,13 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
           mxb = max3(mxb, sacc[qb2][kb][x + 2], sacc[qb2][kb][x + 3]);
         }
       const float mx = max_xor32(__builtin_fmaxf(mxa, mxb));
-      const float cand = Cl[qb2] * mx;
-      // The decision is wave-uniform and usually "keep"; only the scale factor depends on
-      // it and O is always multiplied (by 1 when the max holds).  A branch around the
-      // multiply made the compiler copy all of O on every tile to merge the two paths.
-      const bool up = __any(cand > m[qb2] + kLazy);
-      const float m_new = up ? fmaxf(m[qb2], cand) : m[qb2];
+      // The running max is exact (not lazy): the largest weight computed so far is then
+      // exactly 1 and every weight is at most 1, so rounding P to bf16 perturbs each weight
+      // by at most 2^-9 of itself.  (A lazy max that moved only on jumps of 2^8 let the
+      // dominant weight reach 2^8 and round; O's error then reached 2^-9 max|V|.)  O and
+      // l are multiplied by the factor every tile, 1 when the max holds: a branch around
+      // the multiply made the compiler copy all of O on every tile to merge the two paths.
+      const float m_new = fmaxf(m[qb2], Cl[qb2] * mx);
       const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(m[qb2] - m_new);
       m[qb2] = m_new;
       l[qb2] *= sc;
@@ -365,30 +357,31 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
 #pragma unroll
         for (int x = 0; x < 16; ++x) oacc[qb2][db][x] *= sc;
       const float m_use = (m[qb2] == kNegInf) ? 0.f : m[qb2];
-      // l sums the same fp16-rounded weights the PV product uses (v_dot2 with (1, 1)): O is
-      // normalised by it, an exact convex combination of the rows of V under those weights,
-      // and lse comes from it too (each weight is within 2^-11 of its fp32 value).
-      float ls[2] = {0.f, 0.f};
+      // P is rounded to bf16 for the PV product; l sums the unrounded fp32 weights, so lse
+      // carries only fp32 rounding and O's error is that of the bf16 weights alone.
+      // (the tile's weights are summed from zero, then added to l: accumulated one by one
+      // onto a running l near 1, tiny tail weights would each round by a fixed bias)
+      float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; x += 2) {
           const float p0 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x], -m_use));
           const float p1 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x + 1], -m_use));
-          const uint32_t pk = pack_f16x2(p0, p1);
-          pf[qb2][2 * kb + (x >> 3)][(x & 7) >> 1] = pk;
-          ls[(x >> 1) & 1] = sum_f16x2(pk, ls[(x >> 1) & 1]);
+          pf[qb2][2 * kb + (x >> 3)][(x & 7) >> 1] = pack_bf16x2(p0, p1);
+          ls += p0 + p1;
         }
-      l[qb2] += ls[0] + ls[1];
+      l[qb2] += ls;
     }
 
-    // The next tile's V is converted between the softmax and the PV product in the 256-row
-    // kernel, and after the PV product in the 128-row one.  There the later wait gives the
-    // loads a whole tile of lead time and the shorter live ranges cut the VGPRs from 141 to
-    // 126 (T = 512 and 1,024: 2-3% faster; the 256-row kernel was 6-10% slower that way).
-    if constexpr (NQB != 1) convert_next(nx, t);
+    // In the 128-row kernel the wait for the next tile's loads comes after the PV product,
+    // which gives the loads a whole tile of lead time.
+    if constexpr (NQB != 1) wait_next(t);
+    // (128-row kernel: without this scheduling barrier the compiler hoists PV operand reads
+    // into the softmax and exceeds the 128 VGPRs of four waves per SIMD)
+    if constexpr (NQB == 1) __builtin_amdgcn_sched_barrier(0);
 
-    // ---- O^T += V^T P^T (fp16).  The V^T operand of lane (dh, hh) holds keys
+    // ---- O^T += V^T P^T (bf16).  The V^T operand of lane (dh, hh) holds keys
     // {16 st + 4 hh + 0..3, + 8 .. + 11} of column dh: two transposing reads of the
     // row-major V tile (lane i of 16-lane group G reads row key0 + i / 4, columns
     // dh0 + 4 (i % 4) .. + 3, dh0 = 32 db + 16 (G % 2)).
@@ -396,7 +389,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int col = 32 * db + 16 * (G & 1) + 4 * (gi & 3);
-      f16x8 av[4];
+      bf16x8 av[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         s16x4 v0, v1;
@@ -412,17 +405,17 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
         }
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        av[st] = __builtin_bit_cast(f16x8, vv);
+        av[st] = __builtin_bit_cast(bf16x8, vv);
       }
       if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int qb2 = 0; qb2 < NQB; ++qb2)
-          oacc[qb2][db] = mfma32x32x16_f16(av[st], as_f16x8(pf[qb2][st]), oacc[qb2][db]);
+          oacc[qb2][db] = mfma32x32x16(av[st], as_bf16x8(pf[qb2][st]), oacc[qb2][db]);
       if constexpr (MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
     }
-    if constexpr (NQB == 1) convert_next(nx, t);
+    if constexpr (NQB == 1) wait_next(t);
   };
 
   // ---- pipeline prologue.  Q must be in registers before any later tile load is issued
@@ -470,7 +463,6 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       asm volatile("" : "+v"(qw[qb2][ks]));
       qf[qb2][ks] = as_bf16x8(qw[qb2][ks]);
     }
-  convert_v(tA);
   BAM_BARRIER_VMCNT(63);       // publish tile 0
   // every wave has waited for its loads of tile t + 1 (in compute_tile); publish it
   auto advance = [&]() { BAM_BARRIER_VMCNT(63); };
@@ -484,37 +476,40 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
         ring_next(t + 1);
         issue_tile(tB, jb + (t + 1) * kNK);
       }
-      compute_tile(tA, tB, t);
+      compute_tile(tA, t);
       advance();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) {
         ring_next(t + 2);
         issue_tile(tA, jb + (t + 2) * kNK);
       }
-      compute_tile(tB, tA, t + 1);
+      compute_tile(tB, t + 1);
       advance();
     }
   } else {
     // Three stages: tile t is computed while tiles t + 1 and t + 2 load.
     for (int t = 0; t < ntiles; t += 3) {
       if (t + 2 < ntiles) issue_tile(tC, jb + (t + 2) * kNK);
-      compute_tile(tA, tB, t);
+      compute_tile(tA, t);
       advance();
       if (t + 1 >= ntiles) break;
       if (t + 3 < ntiles) issue_tile(tA, jb + (t + 3) * kNK);
-      compute_tile(tB, tC, t + 1);
+      compute_tile(tB, t + 1);
       advance();
       if (t + 2 >= ntiles) break;
       if (t + 4 < ntiles) issue_tile(tB, jb + (t + 4) * kNK);
-      compute_tile(tC, tA, t + 2);
+      compute_tile(tC, t + 2);
       advance();
     }
   }
 
-  // ---- epilogue
+  // ---- epilogue (the lane's query and half are recomputed here in the 128-row kernel, for
+  // the same reason as the load offsets)
+  const int eln = issue_lane();
+  const int eql = eln & 31, ehh = eln >> 5;
 #pragma unroll
   for (int qb2 = 0; qb2 < NQB; ++qb2) {
-    const int i = iw + 32 * qb2 + ql;
+    const int i = iw + 32 * qb2 + eql;
     const float lt = l[qb2] + xor32(l[qb2]);
     if (i < T) {
       const float inv = 1.0f / lt;
@@ -523,7 +518,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int dh0 = 32 * db + 8 * g + 4 * hh;
+          const int dh0 = 32 * db + 8 * g + 4 * ehh;
           const float o0 = oacc[qb2][db][4 * g + 0] * inv, o1 = oacc[qb2][db][4 * g + 1] * inv;
           const float o2 = oacc[qb2][db][4 * g + 2] * inv, o3 = oacc[qb2][db][4 * g + 3] * inv;
           if (a.o_f32) {
@@ -534,7 +529,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
             *(u32x2*)((uint16_t*)a.o + orow + dh0) = w;
           }
         }
-      if (hh == 0) a.lse[(size_t)bh * T + i] = (m[qb2] + __log2f(lt)) * kLn2;
+      if (ehh == 0) a.lse[(size_t)bh * T + i] = (m[qb2] + __log2f(lt)) * kLn2;
     }
   }
 }

@@ -1,6 +1,11 @@
 """Helpers shared by the GPU parity tests: device copies of the seeded workloads and the
 error measures the tolerances are stated in."""
+import os
+
 import numpy as np
+
+# (test, what, err, tol) of every checked bound, for the run's margin summary (conftest.py)
+MARGINS = []
 
 
 def torch_mod():
@@ -45,3 +50,12 @@ def lse_rel(a, ref):
 F32_REL = 1e-5
 BF16_O_ABS = 1e-2
 BF16_LSE_ABS = 1e-3
+
+
+def within(err, tol, what):
+    """Assert err <= tol with both numbers in the message; record the margin."""
+    err, tol = float(err), float(tol)
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    MARGINS.append((test, what, err, tol))
+    assert err <= tol, f"{what}: err {err:.3e} > tol {tol:.3e}"
+    return err

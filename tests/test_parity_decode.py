@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
+from gpu_util import within
 from gpu_util import BF16_LSE_ABS, BF16_O_ABS, dev, host, max_abs, params, torch_mod
 from positional_prior_bias_amd import workloads as wl
 
@@ -32,8 +33,8 @@ def test_decode_random(L, kv, Dh):
     w = wl.long_decode(seed=40 + L, B=2, H=12, L=L, Dh=Dh, kv_len=np.array(kv))
     o, lse = run_decode(w)
     O, LS = oracle.attn_decode(w.q, w.k, w.v, w.kv_len, w.alpha, w.beta, w.mu, w.s, ssmax=True)
-    assert max_abs(host(o), O) <= BF16_O_ABS
-    assert max_abs(host(lse), LS) <= BF16_LSE_ABS
+    within(max_abs(host(o), O), BF16_O_ABS, "max_abs(host(o), O)")
+    within(max_abs(host(lse), LS), BF16_LSE_ABS, "max_abs(host(lse), LS)")
 
 
 def test_decode_single_key_returns_v0():
@@ -54,8 +55,8 @@ def test_decode_equals_last_prefill_row():
     od, ld = _bam().bam_attn_decode(q[:, :, -1].contiguous(), k, v, kv, p["alpha"], p["beta"], p["mu"], p["s"],
                                     ssmax=True, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert max_abs(host(od), host(o)[:, :, -1]) <= 2 * BF16_O_ABS
-    assert max_abs(host(ld), host(lse)[:, :, -1]) <= 2 * BF16_LSE_ABS
+    within(max_abs(host(od), host(o)[:, :, -1]), 2 * BF16_O_ABS, "max_abs(host(od), host(o)[:, :, -1])")
+    within(max_abs(host(ld), host(lse)[:, :, -1]), 2 * BF16_LSE_ABS, "max_abs(host(ld), host(lse)[:, :, -1])")
 
 
 def test_decode_repeatable_and_bf16_output():
@@ -86,6 +87,5 @@ def test_decode_full_context_256k():
         Ob, Lb = oracle.attn_decode(w.q[b:b + 1], kb, vb, w.kv_len[b:b + 1], w.alpha, w.beta, w.mu, w.s, ssmax=True)
         O[b], LS[b] = Ob[0], Lb[0]
     err_o, err_l = max_abs(host(o), O), max_abs(host(lse), LS)
-    print(f"decode 256k: max|dO|={err_o:.3e} max|dlse|={err_l:.3e}")
-    assert err_o <= BF16_O_ABS
-    assert err_l <= BF16_LSE_ABS
+    within(err_o, BF16_O_ABS, "decode 256k O")
+    within(err_l, BF16_LSE_ABS, "decode 256k lse")

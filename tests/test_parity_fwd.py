@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 import oracle_checks as oc
+from gpu_util import within
 from gpu_util import (BF16_LSE_ABS, BF16_O_ABS, F32_REL, dev, host, lse_rel, max_abs, normwise_rel, params,
                       torch_mod)
 from positional_prior_bias_amd import workloads as wl
@@ -36,8 +37,8 @@ def test_tiny_check_fp32():
     w = wl.tiny_check()
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=False)
-    assert normwise_rel(host(o), O) <= F32_REL
-    assert lse_rel(host(lse), L) <= F32_REL
+    within(normwise_rel(host(o), O), F32_REL, "normwise_rel(host(o), O)")
+    within(lse_rel(host(lse), L), F32_REL, "lse_rel(host(lse), L)")
 
 
 @pytest.mark.parametrize("T,Dh,causal,ssmax", [(1, 32, True, True), (5, 64, False, True), (63, 32, True, False),
@@ -47,8 +48,8 @@ def test_fp32_random(T, Dh, causal, ssmax):
                        mu=-0.5)
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=causal, ssmax=ssmax)
-    assert normwise_rel(host(o), O) <= F32_REL
-    assert lse_rel(host(lse), L) <= F32_REL
+    within(normwise_rel(host(o), O), F32_REL, "normwise_rel(host(o), O)")
+    within(lse_rel(host(lse), L), F32_REL, "lse_rel(host(lse), L)")
 
 
 def test_worked_example_on_gpu():
@@ -67,9 +68,9 @@ def test_worked_example_on_gpu():
     o, _ = _bam().bam_attn_fwd(q, k, v, alpha, beta, None, None, causal=False, ssmax=False, o_dtype=torch.float32)
     out = host(o)[0, :, :, 0]
     expected = 1.0 / (1.0 + np.exp(m))
-    assert max_abs(out[:, 0], expected) <= 1e-6
-    assert max_abs(out[:, 1], 1.0 - expected) <= 1e-6
-    assert max_abs(out[0], [g["head0_pos0"], g["head0_pos1"]]) <= 5e-7
+    within(max_abs(out[:, 0], expected), 1e-6, "max_abs(out[:, 0], expected)")
+    within(max_abs(out[:, 1], 1.0 - expected), 1e-6, "max_abs(out[:, 1], 1.0 - expected)")
+    within(max_abs(out[0], [g["head0_pos0"], g["head0_pos1"]]), 5e-7, 'max_abs(out[0], [g["head0_pos0"], g["head0_pos1"]])')
 
 
 CASES = [
@@ -99,8 +100,8 @@ def test_bf16_random(T, Dh, causal, ssmax, br, mu):
                        mu=mu)
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=causal, ssmax=ssmax)
-    assert max_abs(host(o), O) <= BF16_O_ABS
-    assert max_abs(host(lse), L) <= BF16_LSE_ABS
+    within(max_abs(host(o), O), BF16_O_ABS, "max_abs(host(o), O)")
+    within(max_abs(host(lse), L), BF16_LSE_ABS, "max_abs(host(lse), L)")
 
 
 def test_bf16_alibi_and_nope():
@@ -112,11 +113,13 @@ def test_bf16_alibi_and_nope():
     w.beta = np.ones(H, np.float32)
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=False)
-    assert max_abs(host(o), O) <= BF16_O_ABS and max_abs(host(lse), L) <= BF16_LSE_ABS
+    within(max_abs(host(o), O), BF16_O_ABS, "ALiBi O")
+    within(max_abs(host(lse), L), BF16_LSE_ABS, "ALiBi lse")
     w.alpha = np.full(H, np.inf, np.float32)
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=False)
-    assert max_abs(host(o), O) <= BF16_O_ABS and max_abs(host(lse), L) <= BF16_LSE_ABS
+    within(max_abs(host(o), O), BF16_O_ABS, "NoPE O")
+    within(max_abs(host(lse), L), BF16_LSE_ABS, "NoPE lse")
 
 
 def test_bf16_output_is_rne_of_fp32_and_repeatable():
@@ -136,8 +139,8 @@ def test_training_shape_full():
     o, lse = run_fwd(w)
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=True)
     print(f"training shape: max|dO|={max_abs(host(o), O):.3e} max|dlse|={max_abs(host(lse), L):.3e}")
-    assert max_abs(host(o), O) <= BF16_O_ABS
-    assert max_abs(host(lse), L) <= BF16_LSE_ABS
+    within(max_abs(host(o), O), BF16_O_ABS, "max_abs(host(o), O)")
+    within(max_abs(host(lse), L), BF16_LSE_ABS, "max_abs(host(lse), L)")
 
 
 def long_prefill_rows(T, seed=0, tile=128):
@@ -161,6 +164,5 @@ def test_long_prefill_sampled_rows():
                                     causal=True, ssmax=True)
         worst_o = max(worst_o, max_abs(oh[0, h, rows], O))
         worst_l = max(worst_l, max_abs(lh[0, h, rows], L))
-    print(f"long prefill: {rows.size} rows/head, max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}")
-    assert worst_o <= BF16_O_ABS
-    assert worst_l <= BF16_LSE_ABS
+    within(worst_o, BF16_O_ABS, f"T = 32768 O over {rows.size} rows per head")
+    within(worst_l, BF16_LSE_ABS, f"T = 32768 lse over {rows.size} rows per head")

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+from gpu_util import within
 from gpu_util import BF16_LSE_ABS, BF16_O_ABS, dev, host, max_abs, torch_mod
 from positional_prior_bias_amd import workloads as wl
 
@@ -60,8 +61,8 @@ def _case(w, ssmax=True, prior=None):
     o1, l1, _ = _run(q, k, v, a, b, m, s, ssmax, False, prior)
     o2, l2, frac = _run(q, k, v, a, b, m, s, ssmax, True, prior)
     print(f"skipped fraction {frac:.3f}  |dO| {max_abs(o1, o2):.2e}  |dlse| {max_abs(l1, l2):.2e}")
-    assert max_abs(o1, o2) <= SKIP_EXACT
-    assert max_abs(l1, l2) <= SKIP_EXACT
+    within(max_abs(o1, o2), SKIP_EXACT, "max_abs(o1, o2)")
+    within(max_abs(l1, l2), SKIP_EXACT, "max_abs(l1, l2)")
     return o2, l2, frac
 
 
@@ -78,8 +79,8 @@ def test_skip_local_heads(T, Dh, ssmax):
     o, lse, frac = _case(w, ssmax)
     assert frac > 0.3
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=ssmax)
-    assert max_abs(o, O) <= BF16_O_ABS
-    assert max_abs(lse, L) <= BF16_LSE_ABS
+    within(max_abs(o, O), BF16_O_ABS, "max_abs(o, O)")
+    within(max_abs(lse, L), BF16_LSE_ABS, "max_abs(lse, L)")
 
 
 def test_skip_never_on_inverted_or_nope_heads():
@@ -108,8 +109,8 @@ def test_skip_keeps_a_far_key_that_outweighs_the_prior():
     w.v[0, 0, 3] = 7.0
     o, lse, frac = _case(w)
     O, L = _rows(w, np.array([1999, 2047]))
-    assert max_abs(o[:, :, [1999, 2047]], O) <= BF16_O_ABS
-    assert max_abs(lse[:, :, [1999, 2047]], L) <= BF16_LSE_ABS
+    within(max_abs(o[:, :, [1999, 2047]], O), BF16_O_ABS, "max_abs(o[:, :, [1999, 2047]], O)")
+    within(max_abs(lse[:, :, [1999, 2047]], L), BF16_LSE_ABS, "max_abs(lse[:, :, [1999, 2047]], L)")
     assert o[0, 0, 1999, 0] > 6.0        # the planted key dominates row 1999
 
 
@@ -130,9 +131,11 @@ def test_skip_with_reference_and_sandwich_priors():
                               workspace=ws)
     torch.cuda.synchronize()
     assert bam.fwd_skipped_fraction(ws, 1, H, T, 64, flags) > 0.2
-    assert max_abs(host(o1), host(o2)) <= SKIP_EXACT and max_abs(host(l1), host(l2)) <= SKIP_EXACT
+    within(max_abs(host(o1), host(o2)), SKIP_EXACT, "skipping against full O")
+    within(max_abs(host(l1), host(l2)), SKIP_EXACT, "skipping against full lse")
     O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=True, param="ref")
-    assert max_abs(host(o2), O) <= BF16_O_ABS and max_abs(host(l2), L) <= BF16_LSE_ABS
+    within(max_abs(host(o2), O), BF16_O_ABS, "O")
+    within(max_abs(host(l2), L), BF16_LSE_ABS, "lse")
 
     ws_ = wl.sandwich_case(1901, 1, 3, 700, 64, "bf16")
     _case(ws_, prior="sandwich")
@@ -165,8 +168,9 @@ def test_skip_length_extrapolation_32k():
     o2, l2, frac = _run(q, k, v, a, b, m, s, True, True)
     print(f"32k skipped fraction {frac:.3f}")
     assert frac > 0.05
-    assert max_abs(o1, o2) <= SKIP_EXACT and max_abs(l1, l2) <= SKIP_EXACT
+    within(max_abs(o1, o2), SKIP_EXACT, "T = 32768 skipping against full O")
+    within(max_abs(l1, l2), SKIP_EXACT, "T = 32768 skipping against full lse")
     rows = np.array([0, 1, 4095, 20000, T - 1])
     O, L = _rows(w, rows)
-    assert max_abs(o2[:, :, rows], O) <= BF16_O_ABS
-    assert max_abs(l2[:, :, rows], L) <= BF16_LSE_ABS
+    within(max_abs(o2[:, :, rows], O), BF16_O_ABS, "max_abs(o2[:, :, rows], O)")
+    within(max_abs(l2[:, :, rows], L), BF16_LSE_ABS, "max_abs(l2[:, :, rows], L)")
