@@ -46,7 +46,11 @@
  *   the device cannot be checked without a synchronisation and are preconditions:
  *   alpha > 0 (+inf allowed), beta finite, s > 0, 1 <= kv_len[b] <= Lmax, and for
  *   beta < 0 that d - mu != 0 for every visible distance d (otherwise the bias is -inf
- *   and that key is dropped).
+ *   and that key is dropped).  q, k, v (and dout) must be finite: the kernels are compiled
+ *   on the assumption that no NaN arises (from inputs that meet these preconditions none
+ *   does; masked logits are -inf and no exp2 argument is -inf - -inf), so a NaN or
+ *   infinite input gives undefined values, not necessarily NaN.  A NaN alpha, beta or mu
+ *   likewise; the table entry points make a NaN Sandwich d_bar count as no frequency.
  */
 #ifndef BAM_H
 #define BAM_H
@@ -93,9 +97,10 @@ typedef int bam_status;
  * scaled down per head,
  *   b_h(d) = sum_{i = 0}^{d_bar/2 - 1} cos(d / 10000^(2 i / d_bar)) / ratio_h,
  * with alpha[h] = ratio_h (the page uses 8 (h + 1) / H) and beta[h] = d_bar (the page uses
- * 128); mu is ignored.  The frequency count is trunc(beta[h]) / 2 (none below 2: a zero
- * bias); above 512 frequencies, or for a NaN beta[h], the bias is NaN.  The bias has no parameters: the backward's dalpha, dbeta and dmu are
- * zero.  Not combinable with BAM_PRIOR_REF (BAM_EINVAL).  Accepted by every entry point. */
+ * 128); mu is ignored.  d_bar above 8192 is taken as 8192 (frequencies included), and the
+ * frequency count is trunc(d_bar) / 2: none below 2 (a zero bias).  The bias has no parameters: the
+ * backward's dalpha, dbeta and dmu are zero.  Not combinable with BAM_PRIOR_REF
+ * (BAM_EINVAL).  Accepted by every entry point. */
 #define BAM_PRIOR_SANDWICH 16u
 /* Prior-aware key skipping (bam_attn_fwd, causal bf16 only; BAM_EUNSUPPORTED otherwise).
  * For each block of query rows the call first bounds every logit from above,
@@ -189,7 +194,9 @@ bam_status bam_fwd_skip_plan_offset(int B, int H, int T, int Dh, unsigned flags,
  * int32[B].  The cache already holds the current token, so the query of sequence b sits
  * at position i = kv_len[b] - 1 and sees keys 0 .. kv_len[b] - 1 (causal is implied;
  * n = kv_len[b] for SSMax).  o: [B, H, Dh] of o_dtype; lse: [B, H] float32.
- * flags: BAM_SSMAX only.  Supported: in_dtype BAM_BF16 with Dh in {64, 128}.
+ * flags: BAM_SSMAX, BAM_TABLE_READY and one of BAM_PRIOR_REF / BAM_PRIOR_SANDWICH;
+ * BAM_CAUSAL is accepted and changes nothing (decode is causal by construction).
+ * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128}.
  * The key range is cut into splits processed in parallel and merged exactly by their
  * log-sum-exp; the result does not depend on the split count beyond float rounding.
  */

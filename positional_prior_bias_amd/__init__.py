@@ -1,9 +1,10 @@
 """BAM attention on AMD Instinct MI355X (gfx950): Python binding of libbam.so.
 
 The functions here carry the C entry points' names (include/bam.h) and only
-marshal arguments: they check tensor placement, allocate outputs and the
-workspace with torch, and pass raw device pointers plus torch's current HIP
-stream to the library.  Every step of the computation runs in the library's
+marshal arguments: they check every tensor argument's shape, dtype and device
+against what the kernels will address (raising BamError before anything is
+launched), allocate outputs and the workspace with torch, and pass raw device
+pointers plus torch's current HIP stream to the library.  Every step of the computation runs in the library's
 HIP kernels; there is no fallback path.  If libbam.so has not been built the
 first call raises.
 """
@@ -148,16 +149,50 @@ def _stream(stream=None):
     return stream.cuda_stream
 
 
-def _params(alpha, beta, mu, s, flags):
+def _expect(t, name, shape=None, dtypes=None, device=None):
+    """Check a tensor argument's shape, dtype and device against what the kernels will
+    address (a mismatch would become an out-of-bounds access on the GPU)."""
+    if t is None:
+        raise BamError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise BamError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise BamError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if device is not None and t.device != device:
+        raise BamError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _shape(t, name, ndim):
+    if t is None or t.dim() != ndim:
+        raise BamError(f"{name} must be a {ndim}-D tensor")
+    return tuple(t.shape)
+
+
+def _check_params(alpha, beta, mu, s, flags, H, device):
+    """The per-head prior arrays: float32 with H entries on the data's device (mu may be
+    None; s is required with SSMax and otherwise ignored)."""
+    f32 = (_torch().float32,)
     for name, t in (("alpha", alpha), ("beta", beta)):
-        if t is None or t.dtype != _torch().float32:
-            raise BamError(f"{name} must be a float32 device tensor of length H")
-    return _dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), _dev(s, "s") if (flags & BAM_SSMAX) else _ptr(s)
+        _expect(t, name, shape=(H,), dtypes=f32, device=device)
+    if mu is not None:
+        _expect(mu, "mu", shape=(H,), dtypes=f32, device=device)
+    if flags & BAM_SSMAX:
+        _expect(s, "s", shape=(H,), dtypes=f32, device=device)
+    elif s is not None:
+        _expect(s, "s", shape=(H,), dtypes=f32, device=device)
+
+
+def _param_ptrs(alpha, beta, mu, s):
+    return _dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), _dev(s, "s")
 
 
 def _workspace(nbytes, device, workspace=None):
     torch = _torch()
     if workspace is not None:
+        _expect(workspace, "workspace", device=device)
+        if not workspace.is_contiguous():
+            raise BamError("workspace must be contiguous")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise BamError("workspace too small")
         return workspace
@@ -217,12 +252,13 @@ def bam_bwd_workspace_size(B, H, T, Dh, flags) -> int:
 def bam_prior_table(alpha, beta, mu, d0: int, n: int, derivatives: bool = False, stream=None):
     """tab[h, t] = b_h(d0 + t) (float32 [H, n]); with derivatives also db/dalpha, db/dbeta."""
     torch = _torch()
-    H = alpha.numel()
+    H = _shape(alpha, "alpha", 1)[0]
+    _check_params(alpha, beta, mu, None, 0, H, alpha.device)
+    a, b, m, _ = _param_ptrs(alpha, beta, mu, None)
     tab = torch.empty((H, n), dtype=torch.float32, device=alpha.device)
     da = torch.empty_like(tab) if derivatives else None
     db = torch.empty_like(tab) if derivatives else None
-    st = lib().bam_prior_table(_dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), H, d0, n,
-                               _ptr(tab), _ptr(da), _ptr(db), _stream(stream))
+    st = lib().bam_prior_table(a, b, m, H, d0, n, _ptr(tab), _ptr(da), _ptr(db), _stream(stream))
     _check(st, "bam_prior_table")
     return (tab, da, db) if derivatives else tab
 
@@ -231,10 +267,12 @@ def bam_prior_table_ex(alpha, beta, mu, d0: int, n: int, prior_ref: bool = False
     """(tab, dalpha, dbeta, dmu), each float32 [H, n]: the bias of distance d0 + t and its
     derivatives in the three per-head parameters (theta's with prior_ref)."""
     torch = _torch()
-    H = alpha.numel()
+    H = _shape(alpha, "alpha", 1)[0]
+    flags = _prior_flag(prior_ref, prior)
+    _check_params(alpha, beta, mu, None, 0, H, alpha.device)
+    a, b, m, _ = _param_ptrs(alpha, beta, mu, None)
     outs = [torch.empty((H, n), dtype=torch.float32, device=alpha.device) for _ in range(4)]
-    st = lib().bam_prior_table_ex(_dev(alpha, "alpha"), _dev(beta, "beta"), _dev(mu, "mu"), H, d0, n,
-                                  _prior_flag(prior_ref, prior), *(_ptr(t) for t in outs), _stream(stream))
+    st = lib().bam_prior_table_ex(a, b, m, H, d0, n, flags, *(_ptr(t) for t in outs), _stream(stream))
     _check(st, "bam_prior_table_ex")
     return tuple(outs)
 
@@ -278,24 +316,30 @@ def bam_attn_fwd(q, k, v, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
     skip_far: leave out the leading key tiles whose weights are zero in float32 (BAM_SKIP_FAR;
     causal bf16 only)."""
     torch = _torch()
-    B, H, T, Dh = q.shape
+    B, H, T, Dh = _shape(q, "q", 4)
     flags = (_flags(causal, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
              | (BAM_SKIP_FAR if skip_far else 0))
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != q.shape or v.shape != q.shape:
-        raise BamError("q, k, v must share shape and dtype")
+    dev = q.device
+    for name, t in (("k", k), ("v", v)):
+        _expect(t, name, shape=q.shape, dtypes=(q.dtype,), device=dev)
+    io = (torch.bfloat16, torch.float32)
     oc = in_code if o_dtype is None else (_dtype_code(torch.empty(0, dtype=o_dtype)))
     if o is None:
-        o = torch.empty((B, H, T, Dh), dtype=_torch_dtype(oc), device=q.device)
+        o = torch.empty((B, H, T, Dh), dtype=_torch_dtype(oc), device=dev)
     else:
+        _expect(o, "o", shape=(B, H, T, Dh), dtypes=io, device=dev)
         oc = _dtype_code(o)
     if lse is None:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    else:
+        _expect(lse, "lse", shape=(B, H, T), dtypes=(torch.float32,), device=dev)
+    _check_params(alpha, beta, mu, s, flags, H, dev)
     nb = bam_fwd_workspace_size(B, H, T, Dh, flags & ~BAM_TABLE_READY)
-    ws = _workspace(nb, q.device, workspace)
-    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    ws = _workspace(nb, dev, workspace)
+    a, b_, m_, s_ = _param_ptrs(alpha, beta, mu, s)
     st = lib().bam_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), in_code, B, H, T, Dh, a, b_, m_, s_,
                             flags, _dev(o, "o"), oc, _dev(lse, "lse"), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream))
@@ -308,23 +352,30 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
                  prior=None):
     """Decode; q [B, H, Dh], caches [B, H, Lmax, Dh], kv_len int32 [B].  Returns (o, lse)."""
     torch = _torch()
-    B, H, Lmax, Dh = k_cache.shape
+    B, H, Lmax, Dh = _shape(k_cache, "k_cache", 4)
     flags = _flags(False, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(k_cache)
-    if kv_len.dtype != torch.int32:
-        raise BamError("kv_len must be int32")
+    dev = k_cache.device
+    _expect(v_cache, "v_cache", shape=k_cache.shape, dtypes=(k_cache.dtype,), device=dev)
+    _expect(q, "q", shape=(B, H, Dh), dtypes=(k_cache.dtype,), device=dev)
+    _expect(kv_len, "kv_len", shape=(B,), dtypes=(torch.int32,), device=dev)
+    io = (torch.bfloat16, torch.float32)
     oc = in_code if o_dtype is None else _dtype_code(torch.empty(0, dtype=o_dtype))
     if o is None:
-        o = torch.empty((B, H, Dh), dtype=_torch_dtype(oc), device=q.device)
+        o = torch.empty((B, H, Dh), dtype=_torch_dtype(oc), device=dev)
     else:
+        _expect(o, "o", shape=(B, H, Dh), dtypes=io, device=dev)
         oc = _dtype_code(o)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        _expect(lse, "lse", shape=(B, H), dtypes=(torch.float32,), device=dev)
+    _check_params(alpha, beta, mu, s, flags, H, dev)
     nb = bam_decode_workspace_size(B, H, Lmax, Dh)
-    ws = _workspace(nb, q.device, workspace)
-    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    ws = _workspace(nb, dev, workspace)
+    a, b_, m_, s_ = _param_ptrs(alpha, beta, mu, s)
     st = lib().bam_attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), in_code,
                                _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
                                _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
@@ -338,24 +389,32 @@ def bam_attn_decode_paged(q, k_pages, v_pages, block_table, kv_len, alpha, beta,
     """Decode on a paged cache: q [B, H, Dh]; k_pages, v_pages [num_pages, H, page_size, Dh];
     block_table int32 [B, max_blocks]; kv_len int32 [B].  Returns (o, lse)."""
     torch = _torch()
-    num_pages, H, page_size, Dh = k_pages.shape
-    B, max_blocks = block_table.shape
+    num_pages, H, page_size, Dh = _shape(k_pages, "k_pages", 4)
+    B, max_blocks = _shape(block_table, "block_table", 2)
     flags = _flags(False, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
     if table_ready and workspace is None:
         raise BamError("table_ready needs the workspace of an earlier call")
     in_code = _dtype_code(k_pages)
-    if kv_len.dtype != torch.int32 or block_table.dtype != torch.int32:
-        raise BamError("kv_len and block_table must be int32")
+    dev = k_pages.device
+    _expect(v_pages, "v_pages", shape=k_pages.shape, dtypes=(k_pages.dtype,), device=dev)
+    _expect(block_table, "block_table", dtypes=(torch.int32,), device=dev)
+    _expect(q, "q", shape=(B, H, Dh), dtypes=(k_pages.dtype,), device=dev)
+    _expect(kv_len, "kv_len", shape=(B,), dtypes=(torch.int32,), device=dev)
+    io = (torch.bfloat16, torch.float32)
     oc = in_code if o_dtype is None else _dtype_code(torch.empty(0, dtype=o_dtype))
     if o is None:
-        o = torch.empty((B, H, Dh), dtype=_torch_dtype(oc), device=q.device)
+        o = torch.empty((B, H, Dh), dtype=_torch_dtype(oc), device=dev)
     else:
+        _expect(o, "o", shape=(B, H, Dh), dtypes=io, device=dev)
         oc = _dtype_code(o)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        _expect(lse, "lse", shape=(B, H), dtypes=(torch.float32,), device=dev)
+    _check_params(alpha, beta, mu, s, flags, H, dev)
     nb = bam_decode_workspace_size(B, H, max_blocks * page_size, Dh)
-    ws = _workspace(nb, q.device, workspace)
-    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
+    ws = _workspace(nb, dev, workspace)
+    a, b_, m_, s_ = _param_ptrs(alpha, beta, mu, s)
     st = lib().bam_attn_decode_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"), in_code,
                                      _dev(block_table, "block_table"), max_blocks, num_pages, page_size,
                                      _dev(kv_len, "kv_len"), B, H, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
@@ -383,21 +442,26 @@ def bam_attn_bwd_ex(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=
 def _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream, prior_ref,
          want_mu, prior=None):
     torch = _torch()
-    B, H, T, Dh = q.shape
+    B, H, T, Dh = _shape(q, "q", 4)
     flags = _flags(causal, ssmax, prior_ref, prior)
     in_code = _dtype_code(q)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _expect(t, name, shape=q.shape, dtypes=(q.dtype,), device=dev)
+    _expect(o, "o", shape=q.shape, dtypes=(torch.bfloat16, torch.float32), device=dev)
+    _expect(lse, "lse", shape=(B, H, T), dtypes=(torch.float32,), device=dev)
     gc = in_code if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
     gdt = _torch_dtype(gc)
+    _check_params(alpha, beta, mu, s, flags, H, dev)
+    ws = _workspace(bam_bwd_workspace_size(B, H, T, Dh, flags), dev, workspace)
+    a, b_, m_, s_ = _param_ptrs(alpha, beta, mu, s)
     dq = torch.empty_like(q, dtype=gdt)
     dk = torch.empty_like(q, dtype=gdt)
     dv = torch.empty_like(q, dtype=gdt)
-    dalpha = torch.empty(H, dtype=torch.float32, device=q.device)
+    dalpha = torch.empty(H, dtype=torch.float32, device=dev)
     dbeta = torch.empty_like(dalpha)
     dmu = torch.empty_like(dalpha) if want_mu else None
     ds = torch.empty_like(dalpha)
-    nb = bam_bwd_workspace_size(B, H, T, Dh, flags)
-    ws = _workspace(nb, q.device, workspace)
-    a, b_, m_, s_ = _params(alpha, beta, mu, s, flags)
     head = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dtype_code(o), _dev(lse, "lse"),
             _dev(dout, "dout"), in_code, B, H, T, Dh, a, b_, m_, s_, flags, _dev(dq, "dq"), _dev(dk, "dk"),
             _dev(dv, "dv"), gc, _dev(dalpha, "dalpha"), _dev(dbeta, "dbeta"))

@@ -6,8 +6,10 @@ Every HIP source under csrc/ is compiled with hipcc for gfx950 only, then linked
 into positional_prior_bias_amd/libbam.so.  Packed fp32 VALU instructions are
 disabled on the device side (``-packed-fp32-ops``); hipcc's host pass prints a
 harmless warning that it does not know that feature.  ``-fno-honor-nans`` lets
-max/min lower to single instructions: no kernel here produces a NaN (masked
-logits are -inf and every exp2 argument is guarded against -inf - -inf).
+max/min lower to single instructions: no kernel here produces a NaN from inputs
+that meet include/bam.h's preconditions (finite q, k, v and parameters): masked
+logits are -inf, every exp2 argument is guarded against -inf - -inf, and the
+distance table's entries are finite for finite parameters.
 """
 from __future__ import annotations
 

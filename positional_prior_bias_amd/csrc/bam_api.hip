@@ -237,7 +237,7 @@ DecodeLayout decode_layout(int B, int H, int Lmax, int Dh) {
 }  // namespace
 
 size_t bam_decode_workspace_size(int B, int H, int Lmax, int Dh) {
-  if (B <= 0 || H <= 0 || Lmax <= 0 || (Dh != 64 && Dh != 128)) return 0;
+  if (B <= 0 || H <= 0 || Lmax <= 0 || (Dh != 32 && Dh != 64 && Dh != 128)) return 0;
   return decode_layout(B, H, Lmax, Dh).total;
 }
 
@@ -251,7 +251,7 @@ bam_status decode_common(const void* q, const void* k, const void* v, int in_dty
       lse == nullptr || kv_len == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
   if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | BAM_TABLE_READY | kPriorFlags)) != 0) return BAM_EINVAL;
-  if (in_dtype != BAM_BF16 || (Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
+  if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
   if (o_dtype != BAM_BF16 && o_dtype != BAM_F32) return BAM_EUNSUPPORTED;
   const DecodeLayout L = decode_layout(B, H, Lmax, Dh);
   if (workspace_bytes < L.total) return BAM_EWORKSPACE;

@@ -10,8 +10,8 @@
 //   * grid = (nsplit, H, B); a work-group of 4 waves owns one contiguous key range of
 //     one (b, h) and each wave takes every fourth tile of it;
 //   * a tile is 8 fully coalesced 1 KiB loads of K and of V per wave (16-byte loads,
-//     lane l reads bytes 16 l .. 16 l + 15 of each KiB); Dh / 8 lanes share a key, each
-//     holding 8 of its head-dimension entries;
+//     lane l reads bytes 16 l .. 16 l + 15 of each KiB); Dh / 8 lanes share a key (4, 8 or
+//     16 for Dh = 32, 64, 128), each holding 8 of its head-dimension entries;
 //   * q.k is a per-lane 8-term dot plus a butterfly over the lanes of a key; the
 //     online softmax keeps (m, l, o) per lane with a wave-uniform running max;
 //   * the partial (m, l, o) of each range goes to the workspace and a second kernel
@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
 // unrolled), then combine through LDS.
 template <int DH>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
-  constexpr int EPL = DH / 64;   // head-dim entries per lane
+  constexpr int EPL = (DH + 63) / 64;   // head-dim entries per lane (at Dh = 32 lanes 32..63 idle)
   __shared__ float smax[4];
   __shared__ float sl[4];
   __shared__ float so[4][DH];
@@ -223,11 +223,13 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
     const float wt = (ms == kNegInf) ? 0.f : exp2_fast(ms - M);
     L = fmaf(wt, ps[1], L);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) O[e] = fmaf(wt, ps[2 + lane + 64 * e], O[e]);
+    for (int e = 0; e < EPL; ++e)
+      if (lane + 64 * e < DH) O[e] = fmaf(wt, ps[2 + lane + 64 * e], O[e]);
   }
   if (lane == 0) sl[wave] = L;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) so[wave][lane + 64 * e] = O[e];
+  for (int e = 0; e < EPL; ++e)
+    if (lane + 64 * e < DH) so[wave][lane + 64 * e] = O[e];
   __syncthreads();
   if (tid < DH) {
     const float Ls = sl[0] + sl[1] + sl[2] + sl[3];
@@ -272,6 +274,7 @@ int decode_chunk_keys(int Lmax, int Dh, int BH) {
 
 hipError_t launch_decode(const DecodeArgs& a, int Dh, hipStream_t stream) {
   switch (Dh) {
+    case 32: return launch_t<32>(a, stream);
     case 64: return launch_t<64>(a, stream);
     case 128: return launch_t<128>(a, stream);
     default: return hipErrorInvalidValue;

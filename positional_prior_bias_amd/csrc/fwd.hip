@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
 
   // Q^T operands: lane holds q_i[16 ks + 8 hh .. + 7] of its query in each block
   bf16x8 qf[NQB][KS];
-  float Cl[NQB], m[NQB], l[NQB];
+  float Cl[NQB], m[NQB], mu[NQB], l[NQB];
   const float sqrtD = __builtin_sqrtf((float)DH);
   const float sh = a.ssmax ? a.s[h] : 1.0f;
   u32x4 qw[NQB][KS];
@@ -151,6 +151,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     // logit in log2 units = Cl * (q.k + sqrt(Dh) b); c = 0 only when one key is visible
     Cl[qb2] = fmaxf(c * kLog2e / sqrtD, FLT_MIN);
     m[qb2] = kNegInf;
+    mu[qb2] = 0.f;
     l[qb2] = 0.f;
   }
   f32x16 oacc[NQB][DB];
@@ -348,15 +349,24 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       // dominant weight reach 2^8 and round; O's error then reached 2^-9 max|V|.)  O and
       // l are multiplied by the factor every tile, 1 when the max holds: a branch around
       // the multiply made the compiler copy all of O on every tile to merge the two paths.
+      //
+      // The weights are exp2(fma(Cl, s, -mu)) with mu the exponent reference of the row.  The
+      // running max m = round(Cl * max s) differs from the exact product by up to half an
+      // ulp of m, which is large when a tile of far keys carries a huge bias (at
+      // |m| = 2^34 the max element's exponent could reach +2^9 and its weight overflow).
+      // mu = m + 2^-22 |m| lies above every exact product, so every weight is at most 1 at
+      // any magnitude; below |m| = 2^13 the dominant weight still rounds to exactly 1.
       const float m_new = fmaxf(m[qb2], Cl[qb2] * mx);
-      const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(m[qb2] - m_new);
+      const float mu_new = (m_new == kNegInf) ? 0.f : fmaf(fabsf(m_new), 0x1p-22f, m_new);
+      const float sc = (m[qb2] == kNegInf) ? 0.f : exp2_fast(mu[qb2] - mu_new);
       m[qb2] = m_new;
+      mu[qb2] = mu_new;
       l[qb2] *= sc;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int x = 0; x < 16; ++x) oacc[qb2][db][x] *= sc;
-      const float m_use = (m[qb2] == kNegInf) ? 0.f : m[qb2];
+      const float m_use = mu_new;
       // P is rounded to bf16 for the PV product; l sums the unrounded fp32 weights, so lse
       // carries only fp32 rounding and O's error is that of the bf16 weights alone.
       // (the tile's weights are summed from zero, then added to l: accumulated one by one
@@ -529,7 +539,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
             *(u32x2*)((uint16_t*)a.o + orow + dh0) = w;
           }
         }
-      if (ehh == 0) a.lse[(size_t)bh * T + i] = (m[qb2] + __log2f(lt)) * kLn2;
+      if (ehh == 0) a.lse[(size_t)bh * T + i] = (mu[qb2] + __log2f(lt)) * kLn2;
     }
   }
 }

@@ -24,10 +24,11 @@ namespace bam {
 // parameterisation ("Bayesian Attention Mechanism", "Implementation Details"), where
 // alpha / beta / mu hold theta_alpha / theta_beta / theta_mu, x = (j - i) - mu = -d - mu,
 // mu = e^theta_mu - e^-theta_mu and b = -e^theta_alpha (|x| + eps)^theta_beta;
-// kPriorSandwich: alpha holds ratio_h and beta d_bar (the frequency count is
-// trunc(d_bar) / 2, at most kSandwichMaxFreq; beyond that the entries are NaN), and the
-// derivative tables are zero.
-constexpr int kSandwichMaxFreq = 512;
+// kPriorSandwich: alpha holds ratio_h and beta d_bar (d_bar above 2 kSandwichMaxFreq is
+// taken as 2 kSandwichMaxFreq, and the frequency count is trunc(d_bar) / 2; a NaN d_bar
+// violates the precondition of finite parameters and counts as no frequency, so every
+// entry is finite), and the derivative tables are zero.
+constexpr int kSandwichMaxFreq = 4096;
 
 // u^e for u > 0: the exponent y = e log2(u) in float64, split into an integer n and a
 // fraction f in [0, 1); 2^f in float32 (one v_exp_f32, about 1 ulp), scaled by 2^n
@@ -54,16 +55,18 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
                                                           float* __restrict__ tm) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
-  // Sandwich: the inverse frequencies 10000^(2 i / d_bar) of this head, once per block.
-  __shared__ double inv_w[kSandwichMaxFreq];
+  // Sandwich: the inverse frequencies 10000^(2 i / d_bar) of this head, once per block, in
+  // dynamic LDS (kSandwichMaxFreq doubles; the launch gives none for the other kinds).
+  extern __shared__ double inv_w[];
   int nf = 0;
   if (kind == kPriorSandwich) {
-    // trunc(d_bar) / 2 frequencies; NaN or huge d_bar counts as too many (NaN entries)
-    const float db = beta[h];
-    const bool nan = (__float_as_uint(db) & 0x7fffffffu) > 0x7f800000u;   // by bits: built with -fno-honor-nans
-    nf = (nan || db >= 4096.0f) ? kSandwichMaxFreq + 1 : (db < 2.0f ? 0 : (int)db / 2);
-    for (int i = threadIdx.x; i < kSandwichMaxFreq && i < nf; i += blockDim.x)
-      inv_w[i] = pow(10000.0, 2.0 * i / (double)beta[h]);
+    // trunc(min(d_bar, 8192)) / 2 frequencies; a NaN d_bar (tested by its bits: the library
+    // is built with -fno-honor-nans) counts as none
+    const float db0 = beta[h];
+    const bool nan = (__float_as_uint(db0) & 0x7fffffffu) > 0x7f800000u;
+    const float db = nan ? 0.f : fminf(db0, 2.0f * kSandwichMaxFreq);   // d_bar above 8192 is taken as 8192
+    nf = db < 2.0f ? 0 : (int)db / 2;
+    for (int i = threadIdx.x; i < nf; i += blockDim.x) inv_w[i] = pow(10000.0, 2.0 * i / (double)db);
     __syncthreads();
   }
   if (t >= n) return;
@@ -82,13 +85,9 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   const bool der = ta || tb || tm;   // derivative tables wanted (the forward's table is bias only)
   double b, da = 0.0, db = 0.0, dm = 0.0;
   if (kind == kPriorSandwich) {
-    if (nf > kSandwichMaxFreq) {
-      b = __builtin_nan("");
-    } else {
-      double acc = 0.0;
-      for (int i = 0; i < nf; ++i) acc += cos((double)d / inv_w[i]);
-      b = acc / a;
-    }
+    double acc = 0.0;
+    for (int i = 0; i < nf; ++i) acc += cos((double)d / inv_w[i]);
+    b = acc / a;
   } else if (kind == kPriorRef) {
     // b = -e^ta g^tb, g = |x| + eps: db/dta = b, db/dtb = b ln g,
     // db/dtm = -b tb sign(x) / g * (e^tm + e^-tm)
@@ -122,10 +121,13 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
       }
     }
   }
+  // The derivatives saturate at +-FLT_MAX: where u^beta overflows float32 the bias is -inf
+  // and the weight exactly 0, and the backward's product 0 * derivative must stay 0.
+  const double kFltMax = 3.4028234663852886e38;
   tab[idx] = (float)(b * scale);
-  if (ta) ta[idx] = (float)da;
-  if (tb) tb[idx] = (float)db;
-  if (tm) tm[idx] = (float)dm;
+  if (ta) ta[idx] = (float)fmin(kFltMax, fmax(-kFltMax, da));
+  if (tb) tb[idx] = (float)fmin(kFltMax, fmax(-kFltMax, db));
+  if (tm) tm[idx] = (float)fmin(kFltMax, fmax(-kFltMax, dm));
 }
 
 hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int kind, int H,
@@ -139,7 +141,8 @@ hipError_t launch_prior_table_ex(const float* alpha, const float* beta, const fl
                                  int d_first, int step, int n, int stride, int dlo, int dhi, float scale,
                                  float* tab, float* dalpha, float* dbeta, float* dmu, hipStream_t stream) {
   dim3 grid((n + 255) / 256, H);
-  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), 0, stream, alpha, beta, mu, kind, d_first,
+  const size_t lds = kind == kPriorSandwich ? kSandwichMaxFreq * sizeof(double) : 0;
+  hipLaunchKernelGGL(prior_table_kernel, grid, dim3(256), lds, stream, alpha, beta, mu, kind, d_first,
                      step, n, stride, dlo, dhi, scale, tab, dalpha, dbeta, dmu);
   return hipGetLastError();
 }

@@ -56,3 +56,95 @@ def test_skipped_fraction_arithmetic(T, Dh):
     ws[off:off + 4 * cnt] = torch.from_numpy(plan.view(np.uint8))
     expect = plan.sum() / (tiles.sum() * B * H)
     assert abs(bam.fwd_skipped_fraction(ws, B, H, T, Dh, flags) - expect) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------
+# Argument validation: every mismatch the kernels would turn into an out-of-bounds access
+# is refused by the binding before anything is launched.  These run on CPU tensors: the
+# shape / dtype checks come before the device check, so the message names the mismatch.
+# ---------------------------------------------------------------------------------------
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _f32(n):
+    return torch.ones(n, dtype=torch.float32)
+
+
+def _raises(match, fn, *a, **k):
+    with pytest.raises(bam.BamError, match=match):
+        fn(*a, **k)
+
+
+def test_fwd_argument_checks():
+    B, H, T, Dh = 2, 3, 16, 64
+    q, k, v = _t(B, H, T, Dh), _t(B, H, T, Dh), _t(B, H, T, Dh)
+    p = dict(alpha=_f32(H), beta=_f32(H), mu=_f32(H), s=_f32(H))
+    _raises("k has shape", bam.bam_attn_fwd, q, _t(B, H, T + 1, Dh), v, **p)
+    _raises("v has dtype", bam.bam_attn_fwd, q, k, _t(B, H, T, Dh, dtype=torch.float32), **p)
+    _raises("alpha has shape", bam.bam_attn_fwd, q, k, v, **{**p, "alpha": _f32(H + 1)})
+    _raises("beta has dtype", bam.bam_attn_fwd, q, k, v, **{**p, "beta": torch.ones(H, dtype=torch.float64)})
+    _raises("mu has shape", bam.bam_attn_fwd, q, k, v, **{**p, "mu": _f32(1)})
+    _raises("s is required", bam.bam_attn_fwd, q, k, v, **{**p, "s": None})
+    _raises("s has shape", bam.bam_attn_fwd, q, k, v, **{**p, "s": _f32(2 * H)})
+    _raises("o has shape", bam.bam_attn_fwd, q, k, v, **p, o=_t(B, H, T, Dh // 2))
+    _raises("o has dtype", bam.bam_attn_fwd, q, k, v, **p, o=_t(B, H, T, Dh, dtype=torch.float16))
+    _raises("lse has shape", bam.bam_attn_fwd, q, k, v, **p, lse=_t(B, H, T - 1, dtype=torch.float32))
+    _raises("lse has dtype", bam.bam_attn_fwd, q, k, v, **p, lse=_t(B, H, T))
+    _raises("q must be a 4-D", bam.bam_attn_fwd, _t(B, H, T), k, v, **p)
+    _raises("workspace too small", bam.bam_attn_fwd, q, k, v, **p, workspace=_t(8, dtype=torch.uint8))
+    # metadata right: the remaining objection is the device
+    _raises("device tensor", bam.bam_attn_fwd, q, k, v, **p)
+
+
+def test_decode_argument_checks():
+    B, H, L, Dh = 2, 3, 128, 64
+    kc, vc, q = _t(B, H, L, Dh), _t(B, H, L, Dh), _t(B, H, Dh)
+    kv = torch.full((B,), L, dtype=torch.int32)
+    p = dict(alpha=_f32(H), beta=_f32(H), mu=_f32(H), s=_f32(H))
+    _raises("v_cache has shape", bam.bam_attn_decode, q, kc, _t(B, H, L - 64, Dh), kv, **p)
+    _raises("q has shape", bam.bam_attn_decode, _t(B, H, 2 * Dh), kc, vc, kv, **p)
+    _raises("q has dtype", bam.bam_attn_decode, _t(B, H, Dh, dtype=torch.float32), kc, vc, kv, **p)
+    _raises("kv_len has shape", bam.bam_attn_decode, q, kc, vc, torch.full((B - 1,), L, dtype=torch.int32), **p)
+    _raises("kv_len has dtype", bam.bam_attn_decode, q, kc, vc, kv.long(), **p)
+    _raises("o has shape", bam.bam_attn_decode, q, kc, vc, kv, **p, o=_t(B, H, Dh, 1))
+    _raises("lse has shape", bam.bam_attn_decode, q, kc, vc, kv, **p, lse=_t(B * H, dtype=torch.float32))
+    _raises("alpha has shape", bam.bam_attn_decode, q, kc, vc, kv, **{**p, "alpha": _f32(B)})
+    _raises("device tensor", bam.bam_attn_decode, q, kc, vc, kv, **p)
+
+
+def test_paged_decode_argument_checks():
+    P, H, ps, Dh, B, nb = 6, 3, 64, 64, 2, 3
+    kp, vp, q = _t(P, H, ps, Dh), _t(P, H, ps, Dh), _t(B, H, Dh)
+    bt = torch.zeros((B, nb), dtype=torch.int32)
+    kv = torch.full((B,), nb * ps, dtype=torch.int32)
+    p = dict(alpha=_f32(H), beta=_f32(H), mu=_f32(H), s=_f32(H))
+    _raises("v_pages has shape", bam.bam_attn_decode_paged, q, kp, _t(P - 1, H, ps, Dh), bt, kv, **p)
+    _raises("block_table has dtype", bam.bam_attn_decode_paged, q, kp, vp, bt.long(), kv, **p)
+    _raises("block_table must be a 2-D", bam.bam_attn_decode_paged, q, kp, vp, bt.view(-1), kv, **p)
+    _raises("q has shape", bam.bam_attn_decode_paged, _t(B + 1, H, Dh), kp, vp, bt, kv, **p)
+    _raises("kv_len has shape", bam.bam_attn_decode_paged, q, kp, vp, bt, kv[:1], **p)
+    _raises("device tensor", bam.bam_attn_decode_paged, q, kp, vp, bt, kv, **p)
+
+
+def test_bwd_argument_checks():
+    B, H, T, Dh = 2, 3, 16, 64
+    q = _t(B, H, T, Dh)
+    o, lse, do = _t(B, H, T, Dh, dtype=torch.float32), _t(B, H, T, dtype=torch.float32), _t(B, H, T, Dh)
+    p = dict(alpha=_f32(H), beta=_f32(H), mu=_f32(H), s=_f32(H))
+    _raises("dout has shape", bam.bam_attn_bwd, q, q, q, o, lse, _t(B, H, T, Dh + 8), **p)
+    _raises("dout has dtype", bam.bam_attn_bwd, q, q, q, o, lse, do.float(), **p)
+    _raises("o has shape", bam.bam_attn_bwd, q, q, q, o[:, :, :-1], lse, do, **p)
+    _raises("lse has shape", bam.bam_attn_bwd, q, q, q, o, lse[:, :, :-1], do, **p)
+    _raises("lse has dtype", bam.bam_attn_bwd, q, q, q, o, lse.to(torch.bfloat16), do, **p)
+    _raises("k has shape", bam.bam_attn_bwd_ex, q, _t(B, H, T, 32), q, o, lse, do, **p)
+    _raises("v has dtype", bam.bam_attn_bwd, q, q, q.float(), o, lse, do, **p)
+    _raises("s has shape", bam.bam_attn_bwd, q, q, q, o, lse, do, **{**p, "s": _f32(1)})
+    _raises("device tensor", bam.bam_attn_bwd, q, q, q, o, lse, do, **p)
+
+
+def test_prior_table_argument_checks():
+    _raises("beta has shape", bam.bam_prior_table, _f32(4), _f32(3), None, 0, 8)
+    _raises("mu has dtype", bam.bam_prior_table_ex, _f32(4), _f32(4), torch.zeros(4, dtype=torch.int32), 0, 8)
+    _raises("alpha must be a 1-D", bam.bam_prior_table, _f32(4).view(2, 2), _f32(4), None, 0, 8)

@@ -28,7 +28,9 @@ def run_decode(w, o_dtype=None):
 
 
 @pytest.mark.parametrize("L,kv,Dh", [(1, [1, 1], 64), (100, [100, 37], 64), (5000, [5000, 1234], 64),
-                                     (9000, [1, 8999], 128), (20000, [20000, 4097], 64)])
+                                     (9000, [1, 8999], 128), (20000, [20000, 4097], 64),
+                                     (1, [1, 1], 32), (130, [130, 65], 32), (7000, [6999, 2048], 32),
+                                     (20000, [19999, 511], 32)])
 def test_decode_random(L, kv, Dh):
     w = wl.long_decode(seed=40 + L, B=2, H=12, L=L, Dh=Dh, kv_len=np.array(kv))
     o, lse = run_decode(w)

@@ -167,3 +167,36 @@ def test_dominant_key_flat_tail_T32768():
     within(abs(lh[0, 0, T - 1] - closed), BF16_LSE_ABS, "last row lse against ln(e^13.875 + 32767)")
     within(wo, BF16_O_ABS, "O")
     within(wl_, BF16_LSE_ABS, "lse")
+
+
+def test_steep_prior_stays_finite():
+    """beta = 20, alpha = 1: u^beta overflows float32 from |d| of about 84 on, so those
+    biases are -inf (weight exactly 0) and the parameter derivatives saturate; a tile of
+    far keys gives a running max near -2^34, where half an ulp of the max is 2^10.  The
+    forward and the backward must stay finite and match the oracle (in fp64 nothing
+    overflows and those terms are exactly 0)."""
+    torch = torch_mod()
+    T, Dh, H = 300, 64, 2
+    w = wl.random_case(2300, 1, H, T, Dh, "bf16", wl.CAUSAL | wl.SSMAX, with_grad=True)
+    w.alpha[:] = 1.0
+    w.beta[:] = np.array([20.0, 1.0], np.float32)
+    p = params(w)
+    q, k, v, do = (dev(x, "bf16") for x in (w.q, w.k, w.v, w.do))
+    o, lse = _bam().bam_attn_fwd(q, k, v, p["alpha"], p["beta"], p["mu"], p["s"], causal=True, ssmax=True,
+                                 o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = oracle.attn_fwd(w.q, w.k, w.v, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=True)
+    assert np.all(np.isfinite(host(o))) and np.all(np.isfinite(host(lse)))
+    within(max_abs(host(o), O), BF16_O_ABS, "O")
+    within(max_abs(host(lse), L), BF16_LSE_ABS, "lse")
+    g = _bam().bam_attn_bwd_ex(q, k, v, o, lse, do, p["alpha"], p["beta"], p["mu"], p["s"], causal=True,
+                               ssmax=True, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = [host(x) for x in g]
+    assert all(np.all(np.isfinite(x)) for x in got)
+    ref = oracle.attn_bwd(w.q, w.k, w.v, w.do, w.alpha, w.beta, w.mu, w.s, causal=True, ssmax=True)
+    for name, x, A in zip(("dalpha", "dbeta", "dmu", "ds"), got[3:], ("A_alpha", "A_beta", "A_mu", "A_s")):
+        err = np.abs(x - ref[name])
+        tol = 1e-3 * ref[A] + 1e-6
+        h = int(np.argmax(err / tol))
+        within(err[h], tol[h], f"{name} (worst head {h})")

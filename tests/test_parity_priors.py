@@ -48,17 +48,23 @@ def test_prior_table_sandwich(d_bar):
 
 
 def test_prior_table_sandwich_frequency_count_edges():
-    """Above 512 frequencies (d_bar >= 1026, also huge or NaN d_bar) the documented result
-    is NaN; d_bar below 2 keeps no frequency (zero bias, as the oracle's empty sum)."""
-    ratio = np.ones(6, np.float32)
-    dbar = np.array([1024.0, 1026.0, 3e9, np.nan, 1.5, -4.0], np.float32)
-    tab = host(_bam().bam_prior_table_ex(dev(ratio), dev(dbar), None, -3, 7, prior="sandwich")[0])
-    assert np.all(np.isfinite(tab[0]))
-    assert np.all(np.isnan(tab[1:4]))
+    """d_bar above 8192 is taken as 8192 and the frequency count is trunc(d_bar) / 2:
+    d_bar = 1024 and 1026 (513 frequencies) follow the oracle, d_bar = 9000 and 3e9 that of
+    d_bar = 8192; below 2, and for
+    a NaN d_bar (a precondition violation), no frequency is kept (zero bias, as the
+    oracle's empty sum).  Every entry is finite."""
+    ratio = np.ones(7, np.float32)
+    dbar = np.array([1024.0, 1026.0, 9000.0, 3e9, np.nan, 1.5, -4.0], np.float32)
+    d0, n = -40, 81
+    tab = host(_bam().bam_prior_table_ex(dev(ratio), dev(dbar), None, d0, n, prior="sandwich")[0])
+    assert np.all(np.isfinite(tab))
+    d = np.arange(d0, d0 + n)
+    for h, db in ((0, 1024.0), (1, 1026.0), (2, 8192.0), (3, 8192.0)):
+        r = oracle.prior_bias_sandwich(d, 1.0, db)
+        within(max_abs(tab[h], r), 2e-6 * max(1.0, float(np.abs(r).max())), f"sandwich d_bar {dbar[h]}")
     assert not np.any(tab[4:])
-    d = np.arange(-3, 4)
-    for h in (4, 5):
-        assert np.array_equal(oracle.prior_bias_sandwich(d, 1.0, float(dbar[h])), np.zeros(7))
+    for h in (5, 6):
+        assert np.array_equal(oracle.prior_bias_sandwich(d, 1.0, float(dbar[h])), np.zeros(n))
 
 
 def test_sandwich_with_prior_ref_rejected():
