@@ -9,7 +9,8 @@ harmless warning that it does not know that feature.  ``-fno-honor-nans`` lets
 max/min lower to single instructions: no kernel here produces a NaN from inputs
 that meet include/bam.h's preconditions (finite q, k, v and parameters): masked
 logits are -inf, every exp2 argument is guarded against -inf - -inf, and the
-distance table's entries are finite for finite parameters.
+distance table's entries are finite for finite parameters.  Symbols are hidden by
+default: libbam.so exports only the entry points include/bam.h declares.
 """
 from __future__ import annotations
 
@@ -29,6 +30,7 @@ CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-honor-nans",
+    "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -4,7 +4,11 @@
 
 #include <cmath>
 
+// The library is built with -fvisibility=hidden: only the entry points declared in bam.h
+// are exported.
+#pragma GCC visibility push(default)
 #include "../../include/bam.h"
+#pragma GCC visibility pop
 #include "bam_internal.h"
 
 namespace {

@@ -44,6 +44,8 @@ __device__ __forceinline__ double pow_pos(double u, double e, double& l2) {
   return ldexp((double)exp2f((float)(y - n)), (int)n);
 }
 
+namespace {
+
 __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restrict__ alpha,
                                                           const float* __restrict__ beta,
                                                           const float* __restrict__ mu, int kind,
@@ -129,6 +131,8 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   if (tb) tb[idx] = (float)fmin(kFltMax, fmax(-kFltMax, db));
   if (tm) tm[idx] = (float)fmin(kFltMax, fmax(-kFltMax, dm));
 }
+
+}  // namespace
 
 hipError_t launch_prior_table(const float* alpha, const float* beta, const float* mu, int kind, int H,
                               int d0, int n, int stride, float scale, float* tab, float* dalpha,
