@@ -68,6 +68,7 @@ typedef int bam_status;
 #define BAM_EUNSUPPORTED  2
 #define BAM_EWORKSPACE    3
 #define BAM_EHIP          4
+#define BAM_ETOOLARGE     5   /* bam_attn_decode_static: beyond its static scratch buffer */
 
 /* element types */
 #define BAM_BF16 0
@@ -206,6 +207,26 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            const float* alpha, const float* beta, const float* mu, const float* s,
                            unsigned flags, void* o, int o_dtype, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bam_attn_decode_static - bam_attn_decode with no workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing and calls no allocating routine:
+ * the distance table and the split partials live in a static device buffer of
+ * bam_decode_static_max_bytes() bytes (32 MiB) inside the library, of which each device
+ * the library runs on holds its own copy until the process ends.  Requests whose
+ * bam_decode_workspace_size() exceeds that return BAM_ETOOLARGE (the 256,000-token cache
+ * with B = 8, H = 12, Dh = 64 needs 15.5 MB).  Arguments, flags and results are those of
+ * bam_attn_decode (BAM_TABLE_READY refers to the table the previous static call on this
+ * device left behind).  Every call on a device shares that buffer and its contents persist
+ * between calls: calls that overlap on one device (concurrent streams or threads) race and
+ * give undefined results.
+ */
+size_t bam_decode_static_max_bytes(void);
+bam_status bam_attn_decode_static(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                                  const int32_t* kv_len, int B, int H, int Lmax, int Dh,
+                                  const float* alpha, const float* beta, const float* mu, const float* s,
+                                  unsigned flags, void* o, int o_dtype, float* lse, void* stream);
 
 /*
  * bam_attn_decode_paged - bam_attn_decode on a paged KV cache.

@@ -20,7 +20,7 @@ __all__ = [
     "BamError", "lib", "lib_path",
     "bam_prior_table", "bam_prior_table_ex", "bam_attn_fwd", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_attn_bwd",
-    "bam_attn_bwd_ex",
+    "bam_attn_bwd_ex", "bam_attn_decode_static", "bam_decode_static_max_bytes",
     "bam_fwd_workspace_size", "bam_decode_workspace_size", "bam_bwd_workspace_size",
     "EXPORTED_SYMBOLS",
 ]
@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "bam_status_string", "bam_version", "bam_prior_table", "bam_prior_table_ex",
     "bam_fwd_workspace_size", "bam_attn_fwd", "bam_fwd_skip_plan_offset",
     "bam_decode_workspace_size", "bam_attn_decode", "bam_attn_decode_paged",
+    "bam_decode_static_max_bytes", "bam_attn_decode_static",
     "bam_bwd_workspace_size", "bam_attn_bwd", "bam_attn_bwd_ex",
 )
 
@@ -77,6 +78,10 @@ def _declare(L):
     L.bam_attn_decode_paged.restype = i
     L.bam_attn_decode_paged.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp,
                                         sz, vp]
+    L.bam_decode_static_max_bytes.restype = sz
+    L.bam_decode_static_max_bytes.argtypes = []
+    L.bam_attn_decode_static.restype = i
+    L.bam_attn_decode_static.argtypes = [vp, vp, vp, i, vp, i, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp]
     L.bam_bwd_workspace_size.restype = sz
     L.bam_bwd_workspace_size.argtypes = [i, i, i, i, u]
     L.bam_attn_bwd.restype = i
@@ -380,6 +385,34 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
                                _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
                                _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "bam_attn_decode")
+    return o, lse
+
+
+def bam_decode_static_max_bytes() -> int:
+    return int(lib().bam_decode_static_max_bytes())
+
+
+def bam_attn_decode_static(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, ssmax=True, o=None,
+                           lse=None, stream=None, table_ready=False, prior_ref=False, prior=None):
+    """Decode with no workspace (the library's static device buffer): for callers that
+    cannot allocate.  o [B, H, Dh] (bf16 or fp32) and lse [B, H] fp32 must be given, so the
+    call itself allocates nothing.  Calls that overlap on one device race."""
+    torch = _torch()
+    B, H, Lmax, Dh = _shape(k_cache, "k_cache", 4)
+    flags = _flags(False, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
+    in_code = _dtype_code(k_cache)
+    dev = k_cache.device
+    _expect(v_cache, "v_cache", shape=k_cache.shape, dtypes=(k_cache.dtype,), device=dev)
+    _expect(q, "q", shape=(B, H, Dh), dtypes=(k_cache.dtype,), device=dev)
+    _expect(kv_len, "kv_len", shape=(B,), dtypes=(torch.int32,), device=dev)
+    _expect(o, "o", shape=(B, H, Dh), dtypes=(torch.bfloat16, torch.float32), device=dev)
+    _expect(lse, "lse", shape=(B, H), dtypes=(torch.float32,), device=dev)
+    _check_params(alpha, beta, mu, s, flags, H, dev)
+    a, b_, m_, s_ = _param_ptrs(alpha, beta, mu, s)
+    st = lib().bam_attn_decode_static(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), in_code,
+                                      _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"),
+                                      _dtype_code(o), _dev(lse, "lse"), _stream(stream))
+    _check(st, "bam_attn_decode_static")
     return o, lse
 
 

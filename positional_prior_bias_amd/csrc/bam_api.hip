@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 
 // The library is built with -fvisibility=hidden: only the entry points declared in bam.h
 // are exported.
@@ -103,6 +104,7 @@ const char* bam_status_string(bam_status status) {
     case BAM_EUNSUPPORTED: return "unsupported dtype / head size / flags";
     case BAM_EWORKSPACE: return "workspace too small";
     case BAM_EHIP: return "HIP launch error";
+    case BAM_ETOOLARGE: return "problem exceeds the library's static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -299,6 +301,50 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            void* stream) {
   return decode_common(q, k_cache, v_cache, in_dtype, nullptr, 0, 0, 0, kv_len, B, H, Lmax, Dh, alpha, beta, mu, s,
                        flags, o, o_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode with no workspace argument, for callers that cannot allocate: the distance table
+// and the split partials live in this file's static device array.  Its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current) and kept; host
+// code uses only that address, never the array's name.  Every call on a device shares the
+// array: calls that overlap on one device race.  Nothing in it needs to start at zero (the
+// table kernel writes the whole table and every split writes its whole partial record).
+namespace {
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the scratch array on the current device (null on failure).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+size_t bam_decode_static_max_bytes(void) { return kScratchBytes; }
+
+bam_status bam_attn_decode_static(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                                  const int32_t* kv_len, int B, int H, int Lmax, int Dh, const float* alpha,
+                                  const float* beta, const float* mu, const float* s, unsigned flags, void* o,
+                                  int o_dtype, float* lse, void* stream) {
+  if (!dims_ok(B, H, Lmax)) return BAM_EINVAL;
+  if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
+  if (bam_decode_workspace_size(B, H, Lmax, Dh) > kScratchBytes) return BAM_ETOOLARGE;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return BAM_EHIP;
+  return decode_common(q, k_cache, v_cache, in_dtype, nullptr, 0, 0, 0, kv_len, B, H, Lmax, Dh, alpha, beta, mu, s,
+                       flags, o, o_dtype, lse, ws, kScratchBytes, stream);
 }
 
 bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int in_dtype,

@@ -129,3 +129,17 @@ def test_decode_and_bwd_reject_bad_arguments(L):
     assert pg(16, 16, 16, 0, 16, 4, 8, 96, 16, 1, 1, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None) == 2
     assert pg(16, 16, 16, 0, None, 4, 8, 64, 16, 1, 1, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None) == 1
     assert pg(16, 16, 16, 0, 16, 0, 8, 64, 16, 1, 1, 64, 16, 16, None, 16, 2, 16, 1, 16, 256, 1 << 20, None) == 1
+
+
+def test_static_decode_host_checks(L):
+    """bam_attn_decode_static rejects bad sizes and requests beyond its static buffer before
+    touching the device: these calls pass null pointers and never reach a launch."""
+    null = None
+    args = lambda B, H, Lmax, Dh: (null, null, null, 0, null, B, H, Lmax, Dh, null, null, null, null, 2,  # noqa: E731
+                                   null, 1, null, null)
+    assert L.bam_decode_static_max_bytes() == 32 << 20
+    assert L.bam_attn_decode_static(*args(0, 12, 1000, 64)) == 1          # BAM_EINVAL
+    assert L.bam_attn_decode_static(*args(1, 12, 1000, 48)) == 2          # BAM_EUNSUPPORTED
+    assert L.bam_decode_workspace_size(64, 64, 1 << 20, 128) > L.bam_decode_static_max_bytes()
+    assert L.bam_attn_decode_static(*args(64, 64, 1 << 20, 128)) == 5     # BAM_ETOOLARGE
+    assert L.bam_status_string(5).startswith(b"problem exceeds")
