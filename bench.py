@@ -16,8 +16,10 @@ the K and V bytes of the kv_len visible tokens.
 per launch divided by its average launch duration, measured here with HIP events
 around each launch on the stream it runs on.  `traffic` comes from the committed
 rocprofv3 counter summary in profiles/, and is null when the kernel source has changed
-since those counters were taken.  `cpu_baseline` is the fp64 oracle timed on a bounded
-sample of the same workload on this host's cores.
+since those counters were taken.  `cpu_baseline` is the fp64 oracle on this host's
+cores (a process pool of single-threaded workers, one (b, h) head per task): `value` on
+the training-shape forward in full, and per configuration in `configs` (the backward and
+the 256k decode in full, the 32k forward on a row sample).
 """
 from __future__ import annotations
 
@@ -125,6 +127,8 @@ class Timer:
 
 def device_inputs(torch, w, with_grad=False):
     def d(x, bf16=True):
+        if isinstance(x, torch.Tensor):   # drawn on the device already
+            return x
         t = torch.from_numpy(x)
         return (t.to(torch.bfloat16) if bf16 else t.to(torch.float32)).cuda()
     out = dict(q=d(w.q), k=d(w.k), v=d(w.v), alpha=d(w.alpha, False), beta=d(w.beta, False), mu=d(w.mu, False),
@@ -216,9 +220,14 @@ def bench_fwdbwd(torch, bam, w, steps, warmup, timer):
     bwd_ms = timer.per_launch(bwd, max(steps, 10))
     pairs = B * H * T * (T + 1) // 2
     flops = 14.0 * Dh * pairs
+    # algorithmic bytes of one backward call: Q, K, V, O, dO read and dQ, dK, dV written
+    # (bf16, 2 B per element each), lse read (4 B per row); the tables and per-row scalars
+    # (under 1% of it) are left out
+    bwd_bytes = 8 * B * H * T * Dh * 2 + B * H * T * 4
     log(f"[fwdbwd512] step {ms:.4f} ms, bwd call {bwd_ms:.4f} ms")
     return dict(ms=ms, wall_ms=wall, bwd_call_ms=bwd_ms, flops=flops, tflops=flops / ms / 1e9,
-                bwd_tflops=10.0 * Dh * pairs / bwd_ms / 1e9)
+                bwd_tflops=10.0 * Dh * pairs / bwd_ms / 1e9, bwd_bytes=bwd_bytes,
+                bwd_gbs=bwd_bytes / bwd_ms / 1e6)
 
 
 def bench_decode(torch, bam, w, steps, warmup, timer):
@@ -262,16 +271,20 @@ def bench_train_step(torch, w, steps, warmup, timer):
 
 
 def bench_sweep(torch, bam, wl, timer):
-    """Passkey-style length sweep: causal prefill at T = 1k .. 32k (32,768 tokens per batch)
-    and decode against caches of 4k .. 512k tokens (B = 8, one planted key per sequence)."""
+    """Passkey-style length sweep: causal prefill at T = 1k .. 262k (32,768 tokens per batch
+    up to 32k, then B = 1) and decode against caches of 4k .. 512k tokens (B = 8, one planted
+    key per sequence).  Inputs from 64k on are drawn on the device."""
     out = {"prefill": [], "decode": []}
-    for T in (1024, 4096, 16384, 32768):
-        w = wl.long_prefill(T=T, B=max(1, 32768 // T))
-        r = bench_fwd(torch, bam, w, 5, 2, timer, f"sweep fwd T={T}")
-        out["prefill"].append({"T": T, "B": w.q.shape[0], "kernel_ms": round(r["kernel_ms"], 4),
+    for T in (1024, 4096, 16384, 32768, 65536, 131072, 262144):
+        B = max(1, 32768 // T)
+        w = wl.long_prefill(T=T, B=B) if T <= 32768 else wl.long_prefill_device(T=T, B=B)
+        r = bench_fwd(torch, bam, w, 3, 1, timer, f"sweep fwd T={T}")
+        out["prefill"].append({"T": T, "B": B, "kernel_ms": round(r["kernel_ms"], 4),
                                "kernel_TFLOP/s": round(r["kernel_tflops"], 1),
+                               "kernel_pct_mfma_peak": round(100 * r["kernel_tflops"] / PEAK_BF16_TFLOPS, 2),
                                "step_TFLOP/s": round(r["tflops"], 1)})
         del w
+        torch.cuda.empty_cache()
     for L in (4096, 32768, 131072, 262144, 524288):
         w = wl.long_decode_device(L=L)
         r = bench_decode(torch, bam, w, 5, 2, timer)
@@ -293,36 +306,168 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, seconds):
-    """fp64 oracle on whole (b, h) heads of the same batch, in batch order, repeating the
-    batch until `seconds` have elapsed (so a batch that finishes early is timed over several
-    passes rather than one short one)."""
-    import oracle
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host cores, one (b, h) unit per task in a process
+# pool whose workers run single-threaded BLAS.  The pool is started before the GPU is
+# touched and stays idle while the GPU parts run; each CPU leg runs right after its GPU part.
+# ---------------------------------------------------------------------------------------
+
+_SINGLE_THREAD_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+
+
+def _cpu_worker_init():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
-        threads = 1
-    B, H, T, Dh = w.q.shape
-    done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for b in range(B):
-            for h in range(H):
-                oracle.attn_fwd(w.q[b:b + 1, h:h + 1], w.k[b:b + 1, h:h + 1], w.v[b:b + 1, h:h + 1],
-                                w.alpha[h:h + 1], w.beta[h:h + 1], w.mu[h:h + 1], w.s[h:h + 1], causal=True,
-                                ssmax=True)
-                done += 1
-                if time.perf_counter() - t0 >= seconds:
-                    break
-            if time.perf_counter() - t0 >= seconds:
-                break
-    el = time.perf_counter() - t0
-    flops = fwd_flops(1, done, T, Dh)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} (b,h) heads ({done / (B * H):.2f} passes over the B={B},H={H},T={T},Dh={Dh} batch), "
-                      f"every row, {el:.1f} s of fp64 numpy (BLAS threads={threads}, elementwise work "
-                      f"single-threaded) on {_cpu_model()}"}
+        pass
+    import oracle  # noqa: F401  (import cost paid before any task is timed)
+
+
+def _cpu_noop(_):
+    time.sleep(0.05)   # long enough that every worker takes one
+    return os.getpid()
+
+
+def _cpu_task(task):
+    """One (b, h) unit of the oracle: ("fwd" | "fwdbwd" | "rows" | "decode", arrays...)."""
+    import numpy as np
+    import oracle
+    kind = task[0]
+    if kind == "fwd":
+        _, q, k, v, a, b, m, s = task
+        oracle.attn_fwd(q[None, None], k[None, None], v[None, None], [a], [b], [m], [s], causal=True, ssmax=True)
+    elif kind == "fwdbwd":
+        _, q, k, v, do, a, b, m, s = task
+        oracle.attn_fwd(q[None, None], k[None, None], v[None, None], [a], [b], [m], [s], causal=True, ssmax=True)
+        oracle.attn_bwd(q[None, None], k[None, None], v[None, None], do[None, None], [a], [b], [m], [s],
+                        causal=True, ssmax=True)
+    elif kind == "rows":
+        _, q, k, v, rows, a, b, m, s = task
+        oracle.attn_fwd_rows(q, k, v, rows, a, b, m, s, causal=True, ssmax=True)
+    elif kind == "decode":
+        _, q, kbits, vbits, n, a, b, m, s = task
+        widen = lambda x: (x.astype(np.uint32) << 16).view(np.float32)  # noqa: E731  (bf16 bits)
+        oracle.attn_decode(q[None, None], widen(kbits)[None, None], widen(vbits)[None, None], [n], [a], [b], [m],
+                           [s], ssmax=True)
+    return os.getpid()
+
+
+class CpuOracle:
+    """The process pool and the per-configuration oracle timings."""
+
+    def __init__(self, seconds):
+        import multiprocessing as mp
+        self.cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        self.seconds = seconds
+        saved = {k: os.environ.get(k) for k in _SINGLE_THREAD_ENV}
+        for k in _SINGLE_THREAD_ENV:
+            os.environ[k] = "1"
+        try:
+            self.pool = mp.get_context("spawn").Pool(self.cores, initializer=_cpu_worker_init)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        self.pool.map(_cpu_noop, range(2 * self.cores), chunksize=1)
+        self.used = set()   # worker processes that ran timed tasks
+        self.results = {}
+
+    @property
+    def workers(self):
+        return len(self.used) if self.used else self.cores
+
+    def close(self):
+        self.pool.close()
+        self.pool.join()
+
+    def _run(self, tasks):
+        t0 = time.perf_counter()
+        for pid in self.pool.imap_unordered(_cpu_task, tasks):
+            self.used.add(pid)
+        return time.perf_counter() - t0
+
+    def _passes(self, make_tasks):
+        """Whole passes over the batch until `seconds` have elapsed (at least one)."""
+        el, n = 0.0, 0
+        while n == 0 or el < self.seconds:
+            el += self._run(make_tasks())
+            n += 1
+        return el, n
+
+    def fwd_full(self, w):
+        B, H, T, Dh = w.q.shape
+        mk = lambda: [("fwd", w.q[b, h], w.k[b, h], w.v[b, h], w.alpha[h], w.beta[h], w.mu[h], w.s[h])  # noqa: E731
+                      for b in range(B) for h in range(H)]
+        el, n = self._passes(mk)
+        flops = n * fwd_flops(B, H, T, Dh)
+        self.results["fwd_T512"] = {
+            "workload": f"causal fwd B={B} H={H} T={T} Dh={Dh}, every row", "passes": n, "seconds": round(el, 2),
+            "TFLOP/s": flops / el / 1e12}
+        return self.results["fwd_T512"]
+
+    def fwdbwd_full(self, w):
+        B, H, T, Dh = w.q.shape
+        mk = lambda: [("fwdbwd", w.q[b, h], w.k[b, h], w.v[b, h], w.do[b, h], w.alpha[h], w.beta[h], w.mu[h],  # noqa: E731
+                       w.s[h]) for b in range(B) for h in range(H)]
+        el, n = self._passes(mk)
+        flops = n * 14.0 * Dh * B * H * T * (T + 1) / 2
+        self.results["fwd_bwd_T512"] = {
+            "workload": f"causal fwd+bwd B={B} H={H} T={T} Dh={Dh}, every row", "passes": n,
+            "seconds": round(el, 2), "TFLOP/s": flops / el / 1e12}
+
+    def rows_sample(self, w, nrows=256, seed=0):
+        """The T = 32768 forward on a stratified row sample: nrows rows per head, evenly
+        spread over [0, T) (each row costs keys 0..i), extrapolated to every row by the
+        visible-pair count."""
+        import numpy as np
+        B, H, T, Dh = w.q.shape
+        rows = np.unique(np.linspace(0, T - 1, nrows).round().astype(np.int64))
+        tasks = [("rows", w.q[0, h], w.k[0, h], w.v[0, h], rows, w.alpha[h], w.beta[h], w.mu[h], w.s[h])
+                 for h in range(H)]
+        el = self._run(tasks)
+        pairs_sampled = float(H * (rows + 1).sum())
+        rate = 4.0 * Dh * pairs_sampled / el
+        self.results["fwd_T32768"] = {
+            "workload": f"causal fwd B={B} H={H} T={T} Dh={Dh}: {rows.size} rows per head sampled evenly over [0, T)",
+            "seconds": round(el, 2), "TFLOP/s": rate / 1e12,
+            "extrapolated_full_call_s": round(fwd_flops(B, H, T, Dh) / rate, 1),
+            "note": "rate measured on the sampled rows; the full-call time is extrapolated by visible pairs"}
+
+    def decode_full(self, w):
+        """Every (b, h) of the 256,000-token decode: each slab is copied to the host (bf16 bits)
+        and sent to a worker; the copy runs while the pool computes earlier slabs."""
+        import numpy as np
+        import torch
+        B, H, L, Dh = w.k.shape
+
+        def tasks():
+            for b in range(B):
+                n = int(w.kv_len[b])
+                for h in range(H):
+                    kb = w.k[b, h, :n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                    vb = w.v[b, h, :n].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                    yield ("decode", w.q[b, h], kb, vb, n, w.alpha[h], w.beta[h], w.mu[h], w.s[h])
+        el = self._run(tasks())
+        nbytes = 2.0 * float(w.kv_len.astype("int64").sum()) * H * Dh * 2
+        self.results["decode_256k"] = {
+            "workload": f"decode B={B} H={H} L={L} Dh={Dh}, every (b, h), bf16 cache widened on the host",
+            "seconds": round(el, 2), "GB/s": nbytes / el / 1e9,
+            "note": "includes the device-to-host copy of each K/V slab, overlapped with the pool's work"}
+
+    def summary(self):
+        r = self.results.get("fwd_T512")
+        if r is None:
+            return None
+        return {"value": r["TFLOP/s"], "unit": "TFLOP/s", "cores": self.workers, "kind": "oracle",
+                "sample": f"the training-shape forward in full ({r['workload']}), {r['passes']} passes in "
+                          f"{r['seconds']} s: a spawn process pool of {self.workers} workers, one (b, h) head per "
+                          f"task, single-threaded fp64 numpy each, on {_cpu_model()}; per-configuration figures "
+                          f"in configs",
+                "configs": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                            for k, v in self.results.items()}}
 
 
 def traffic_from_counters():
@@ -341,10 +486,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--parts", default="fwd512,fwd32k,skip32k,decode,fwdbwd512,train512",
-                    help="comma list of fwd512,fwd32k,skip32k,decode,fwdbwd512,train512,sweep (fwd512 is "
-                         "always run; skip32k needs fwd32k; sweep, the length sweep, is not run by default)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--parts", default="fwd512,fwd32k,skip32k,decode,fwdbwd512,train512,sweep",
+                    help="comma list of fwd512,fwd32k,skip32k,decode,fwdbwd512,train512,sweep,cold512 (fwd512 is "
+                         "always run; skip32k needs fwd32k; cold512, the T = 512 forward after a cache flush, "
+                         "is not run by default so that every default launch of that kernel is a warm one)")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="minimum time of each whole-batch CPU-baseline leg (the batch is repeated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for scaling HBM counters)")
@@ -355,6 +502,12 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (BAM attention shards with no "
               "exchange over heads/batch; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    parts = set(args.parts.split(",")) | {"fwd512"}
+    # the CPU baseline's worker pool starts before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else CpuOracle(args.cpu_seconds)
+    if cpu is not None:
+        log(f"[cpu_baseline] pool of {cpu.workers} single-threaded workers on {_cpu_model()}")
 
     import numpy as np  # noqa: F401
     import torch
@@ -367,20 +520,23 @@ def main():
         sys.exit(2)
     bam.lib()
     timer = Timer(torch)
-    parts = set(args.parts.split(",")) | {"fwd512"}
 
     log("[fwd512] generating inputs")
     w2 = wl.training_shape()
-    r512 = bench_fwd(torch, bam, w2, args.steps, args.warmup, timer, "fwd512", cold=True)
+    r512 = bench_fwd(torch, bam, w2, args.steps, args.warmup, timer, "fwd512", cold="cold512" in parts)
     out_parts = {"fwd_T512": {
         "workload": "causal fwd B=32 H=12 T=512 Dh=64 bf16, SSMax on",
         "ms": round(r512["ms"], 5), "TFLOP/s": round(r512["tflops"], 2),
         "pct_mfma_peak": round(100 * r512["tflops"] / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": round(r512["kernel_ms"], 5), "kernel_TFLOP/s": round(r512["kernel_tflops"], 2),
         "kernel_algorithmic_GB/s": round(r512["kernel_gbs"], 1),
-        "cold_kernel_ms": round(r512["cold_kernel_ms"], 5),
-        "cold_kernel_TFLOP/s": round(r512["flops"] / r512["cold_kernel_ms"] / 1e9, 2),
         "pct_hbm_peak": round(100 * r512["kernel_gbs"] / PEAK_HBM_GBS, 2)}}
+    if r512["cold_kernel_ms"] is not None:
+        out_parts["fwd_T512"]["cold_kernel_ms"] = round(r512["cold_kernel_ms"], 5)
+        out_parts["fwd_T512"]["cold_kernel_TFLOP/s"] = round(r512["flops"] / r512["cold_kernel_ms"] / 1e9, 2)
+    if cpu is not None:
+        log("[cpu_baseline] training-shape forward")
+        cpu.fwd_full(w2)
 
     if "fwd32k" in parts:
         log("[fwd32k] generating inputs")
@@ -399,6 +555,9 @@ def main():
                 "note": "prior-aware key skipping: same results, less work; effective_TFLOP/s = the dense "
                         "algorithmic flops / the skipping call's time, not the metric",
                 **bench_skip(torch, bam, w4, max(3, args.steps // 4), timer)}
+        if cpu is not None:
+            log("[cpu_baseline] 32k forward, row sample")
+            cpu.rows_sample(w4)
         del w4
     if "decode" in parts:
         log("[decode] generating inputs (256,000-token caches)")
@@ -411,7 +570,11 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(r["kernels_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(r["kernels_gbs"] / PEAK_HBM_GBS, 4),
                          "note": "split + combine kernels (table prebuilt), K+V bytes of the visible tokens"}}
+        if cpu is not None:
+            log("[cpu_baseline] 256k decode, every (b, h)")
+            cpu.decode_full(w5)
         del w5
+        torch.cuda.empty_cache()
     if "fwdbwd512" in parts:
         log("[fwdbwd512] generating inputs")
         w3 = wl.training_shape(with_grad=True)
@@ -420,7 +583,13 @@ def main():
             "workload": "causal fwd+bwd B=32 H=12 T=512 Dh=64 bf16, dQ/dK/dV bf16 + per-head dalpha/dbeta/ds",
             "ms": round(r["ms"], 4), "TFLOP/s": round(r["tflops"], 1),
             "pct_mfma_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
-            "bwd_call_ms": round(r["bwd_call_ms"], 4), "bwd_TFLOP/s": round(r["bwd_tflops"], 1)}
+            "bwd_call_ms": round(r["bwd_call_ms"], 4), "bwd_TFLOP/s": round(r["bwd_tflops"], 1),
+            "bwd_roofline": {"bound": "hbm", "achieved": round(r["bwd_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(r["bwd_gbs"] / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes_per_call": r["bwd_bytes"],
+                             "pct_mfma_peak": round(100 * r["bwd_tflops"] / PEAK_BF16_TFLOPS, 2),
+                             "note": "whole backward call (table + bwd_dq + bwd_dkdv): Q, K, V, O, dO read, "
+                                     "dQ, dK, dV written (bf16) and lse read"}}
         if "train512" in parts:
             r = bench_train_step(torch, w3, args.steps, args.warmup, timer)
             out_parts["train_step_T512"] = {
@@ -428,6 +597,9 @@ def main():
                             "grads for q, k, v, theta_alpha, theta_beta, theta_mu, s",
                 "ms": round(r["ms"], 4), "wall_ms": round(r["wall_ms"], 4),
                 "TFLOP/s": round(14.0 * 64 * 32 * 12 * 512 * 513 / 2 / r["ms"] / 1e9, 1)}
+        if cpu is not None:
+            log("[cpu_baseline] training-shape forward + backward")
+            cpu.fwdbwd_full(w3)
         del w3
 
     if "sweep" in parts:
@@ -451,10 +623,19 @@ def main():
     if traffic is None:
         roof["traffic_note"] = tnote
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"[cpu_baseline] oracle for ~{args.cpu_seconds:.0f} s")
-        cpu = cpu_baseline(w2, args.cpu_seconds)
+    cpu_line = None
+    if cpu is not None:
+        cpu_line = cpu.summary()
+        cpu.close()
+        gpu = {"fwd_T512": out_parts["fwd_T512"].get("kernel_TFLOP/s"),
+               "fwd_T32768": out_parts.get("fwd_T32768", {}).get("kernel_TFLOP/s"),
+               "fwd_bwd_T512": out_parts.get("fwd_bwd_T512", {}).get("TFLOP/s"),
+               "decode_256k": out_parts.get("decode_256k", {}).get("GB/s")}
+        for k, v in cpu_line["configs"].items():
+            g = gpu.get(k)
+            c = v.get("TFLOP/s", v.get("GB/s"))
+            if g and c:
+                v["gpu_over_cpu"] = round(g / c, 1)
 
     line = {
         "metric": METRIC, "value": round(r512["tflops"], 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -464,7 +645,7 @@ def main():
         "config": {"workload": "training-shape causal BAM attention forward, B=32 H=12 T=512 Dh=64, bf16 in/out, "
                                "fp32 accumulate, SSMax on; one step = bam_attn_fwd (distance table + attention)",
                    "B": 32, "H": 12, "T": 512, "Dh": 64, "parallelism": "single GPU"},
-        "roofline": roof, "cpu_baseline": cpu, "parts": out_parts,
+        "roofline": roof, "cpu_baseline": cpu_line, "parts": out_parts,
     }
     print(json.dumps(line), flush=True)
 

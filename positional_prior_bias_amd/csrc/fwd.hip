@@ -81,8 +81,11 @@ static_assert(kRingStride >= kRingEntries && kRingStride % 32 == 16, "ring copie
 
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
-template <int DH, bool CAUSAL, int NQB>
+// SKIP: the launch carries a prior-aware skipping plan (causal only); a separate
+// instantiation, so profiles tell skipping launches from full ones.
+template <int DH, bool CAUSAL, int NQB, bool SKIP>
 __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_kernel(FwdArgs a, int nqb) {
+  static_assert(CAUSAL || !SKIP, "skipping plans are causal only");
   constexpr int QW = 32 * NQB;          // query rows per wave
   constexpr int MQ = 4 * QW;            // query rows per work-group
   constexpr int TW = MQ + kNK;          // distance-window entries per tile (multiple of 64)
@@ -165,7 +168,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   const int kend = CAUSAL ? min(T, i0 + MQ) : T;
   // key tiles before tf carry no weight float32 can hold (prior-aware plan; causal only)
   int tf = 0;
-  if (CAUSAL && a.first_tile)
+  if (SKIP && a.first_tile)
     tf = min(max(__builtin_amdgcn_readfirstlane(a.first_tile[qb * BH + bh]), 0), i0 / kNK);
   const int jb = tf * kNK;                          // first key of the loop
   const int ntiles = (kend - jb + kNK - 1) / kNK;   // tiles from jb on
@@ -663,7 +666,14 @@ hipError_t launch_bf16_nqb(const FwdArgs& a, hipStream_t stream) {
   constexpr int MQ = 4 * 32 * NQB;
   const int nqb = (a.T + MQ - 1) / MQ;
   const long nblocks = (long)nqb * a.B * a.H;
-  hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL, NQB>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, nqb);
+  if constexpr (CAUSAL) {
+    if (a.first_tile != nullptr) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL, NQB, true>), dim3((unsigned)nblocks), dim3(256), 0, stream, a,
+                         nqb);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<DH, CAUSAL, NQB, false>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, nqb);
   return hipGetLastError();
 }
 

@@ -310,3 +310,30 @@ def long_decode_device(seed: int = 4, B: int = 8, H: int = 12, L: int = 256000, 
     alpha, beta, mu, s = extrapolation_heads(hrng, H)
     return Workload("decode_L%d_device" % L, B, H, L, Dh, "bf16", SSMAX, alpha, beta, mu, s, q, k, v,
                     kv_len=kv_len, planted=planted)
+
+
+def long_prefill_heads(H: int = 12, Dh: int = 64, seed: int = 3):
+    """The head parameters of the 32,768-token prefill (drawn after its Q, K, V from `seed`)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(3):
+        rng.standard_normal(size=(1, H, 32768, Dh), dtype=np.float32)
+    return extrapolation_heads(rng, H)
+
+
+def long_prefill_device(seed: int = 3, B: int = 1, H: int = 12, T: int = 262144, Dh: int = 64,
+                        device="cuda") -> Workload:
+    """Length-sweep prefill with Q, K, V drawn directly on the GPU (lengths past 32k).
+
+    Q, K, V ([B, H, T, Dh], bf16) come from torch's counter-based Philox generator on
+    `device`, seeded with `seed`: one float32 randn draw of (B, H, T, Dh) each, in that
+    order, rounded to bf16.  The head parameters are those of the 32,768-token prefill
+    (long_prefill_heads), so every length of the sweep runs the same heads.  The returned
+    workload's q, k and v are torch device tensors.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    qkv = [torch.randn((B, H, T, Dh), generator=gen, dtype=torch.float32, device=device).to(torch.bfloat16)
+           for _ in range(3)]
+    alpha, beta, mu, s = long_prefill_heads(H, Dh, 3)
+    return Workload("prefill_T%d_device" % T, B, H, T, Dh, "bf16", CAUSAL | SSMAX, alpha, beta, mu, s, *qkv)
