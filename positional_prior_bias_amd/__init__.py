@@ -11,6 +11,7 @@ first call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 __all__ = [
@@ -114,9 +115,15 @@ def _check(status: int, what: str):
 # torch marshalling helpers
 # ---------------------------------------------------------------------------------------
 
+_TORCH = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 def _dtype_code(t) -> int:
@@ -159,7 +166,7 @@ def _expect(t, name, shape=None, dtypes=None, device=None):
     address (a mismatch would become an out-of-bounds access on the GPU)."""
     if t is None:
         raise BamError(f"{name} is required")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise BamError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtypes is not None and t.dtype not in dtypes:
         raise BamError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
@@ -242,14 +249,17 @@ def alibi_slopes(n_heads, device=None):
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------------------
 
+@functools.lru_cache(maxsize=256)
 def bam_fwd_workspace_size(B, H, T, Dh, flags) -> int:
     return int(lib().bam_fwd_workspace_size(B, H, T, Dh, flags))
 
 
+@functools.lru_cache(maxsize=256)
 def bam_decode_workspace_size(B, H, Lmax, Dh) -> int:
     return int(lib().bam_decode_workspace_size(B, H, Lmax, Dh))
 
 
+@functools.lru_cache(maxsize=256)
 def bam_bwd_workspace_size(B, H, T, Dh, flags) -> int:
     return int(lib().bam_bwd_workspace_size(B, H, T, Dh, flags))
 
