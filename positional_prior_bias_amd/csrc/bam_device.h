@@ -31,40 +31,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1), fp32 accumulate)
-__device__ __forceinline__ float sum_bf16x2(uint32_t packed, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
-}
-
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f32x16 mfma32x32x16_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
-
-// two floats -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const f16x2 v = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// acc + lo + hi of a packed fp16 pair (v_dot2_f32_f16 against (1, 1), fp32 accumulate)
-__device__ __forceinline__ float sum_f16x2(uint32_t packed, float acc) {
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
-}
-
-// a packed bf16 pair -> the same two values as a packed fp16 pair (exact for magnitudes
-// in [2^-14, 65504]; below that fp16 keeps fewer bits, above it the value overflows)
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
