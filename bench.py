@@ -251,6 +251,44 @@ def bench_decode(torch, bam, w, steps, warmup, timer):
                 kernels_gbs=nbytes / kern_ms / 1e6)
 
 
+def bench_decode_skip(torch, bam, w, steps, timer, full_kernels_ms):
+    """Prior-aware decode skipping on the same workload: the key-norm pages (built once per
+    cache change), the skipping call's kernels with the table prebuilt (bound + split +
+    combine), the fraction of key ranges left out, and whether the output has the full
+    call's bits."""
+    B, H, L, Dh = w.k.shape
+    q = torch.from_numpy(w.q).to(torch.bfloat16).cuda()
+    kv = torch.from_numpy(w.kv_len).cuda()
+    p = {n: torch.from_numpy(getattr(w, n)).cuda() for n in ("alpha", "beta", "mu", "s")}
+    ws = torch.empty(bam.bam_decode_workspace_size(B, H, L, Dh), dtype=torch.uint8, device="cuda")
+    norms = torch.empty((B, H, bam.bam_decode_norm_pages(L)), dtype=torch.float32, device="cuda")
+    norms_ms = timer.per_launch(lambda: bam.bam_decode_key_norms(w.k, norms=norms), 10)
+    o_full, l_full = bam.bam_attn_decode(q, w.k, w.v, kv, p["alpha"], p["beta"], p["mu"], p["s"], ssmax=True,
+                                         o_dtype=torch.float32, workspace=ws)
+    o_full, l_full = o_full.clone(), l_full.clone()
+    o = torch.empty((B, H, Dh), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+
+    def call(table_ready=True):
+        bam.bam_attn_decode_skip(q, w.k, w.v, kv, p["alpha"], p["beta"], p["mu"], p["s"], key_norms=norms, ssmax=True,
+                                 o=o, lse=lse, workspace=ws, table_ready=table_ready)
+    call(False)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o.view(torch.int32), o_full.view(torch.int32)) and
+                torch.equal(lse.view(torch.int32), l_full.view(torch.int32)))
+    frac = bam.decode_skipped_fraction(ws, kv, B, H, L, Dh)
+    kern_ms = timer.per_launch(call, max(steps, 10))
+    nbytes = 2.0 * float(w.kv_len.astype("int64").sum()) * H * Dh * 2
+    log(f"[decode skip] ranges skipped {frac:.3f}, kernels {kern_ms:.4f} ms (full {full_kernels_ms:.4f}), "
+        f"norm pages {norms_ms:.4f} ms, same bits {same}")
+    return {"note": "prior-aware decode skipping: the same bits as the full call, less work; effective_GB/s = the "
+                    "dense K+V bytes / the skipping kernels' time, not the metric",
+            "skipped_range_fraction": round(frac, 4), "same_bits_as_full": same,
+            "full_kernels_ms": round(full_kernels_ms, 4), "skip_kernels_ms": round(kern_ms, 4),
+            "speedup": round(full_kernels_ms / kern_ms, 3), "effective_GB/s": round(nbytes / kern_ms / 1e6, 1),
+            "key_norm_pages_ms": round(norms_ms, 4)}
+
+
 def bench_train_step(torch, w, steps, warmup, timer):
     """Forward + backward through the autograd module (reference parameterisation, every
     prior parameter trained, SSMax on), gradients for q, k, v and the prior."""
@@ -570,6 +608,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(r["kernels_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(r["kernels_gbs"] / PEAK_HBM_GBS, 4),
                          "note": "split + combine kernels (table prebuilt), K+V bytes of the visible tokens"}}
+        out_parts["decode_256k"]["skip"] = bench_decode_skip(torch, bam, w5, max(5, args.steps // 2), timer,
+                                                             r["kernels_ms"])
         if cpu is not None:
             log("[cpu_baseline] 256k decode, every (b, h)")
             cpu.decode_full(w5)

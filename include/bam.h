@@ -209,6 +209,52 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bam_decode_partials_layout - where a decode call on a workspace of
+ * bam_decode_workspace_size(B, H, Lmax, Dh) bytes leaves its per-range partials: float32
+ * records [B, H, nsplit, Dh + 2] = (m, l, o[Dh]) from byte *offset, key range s covering
+ * keys s * chunk .. s * chunk + chunk - 1.  A range with no visible key, and a range that
+ * bam_attn_decode_skip left out, has m = -inf.  BAM_EINVAL for unsupported sizes or NULL
+ * outputs.
+ */
+bam_status bam_decode_partials_layout(int B, int H, int Lmax, int Dh, size_t* offset, int* nsplit, int* chunk);
+
+/*
+ * bam_decode_key_norms - per-page maxima of the key norms of a contiguous KV cache, the
+ * companion array that bam_attn_decode_skip reads.  Pages are 64 keys: norms (device
+ * float32, [B, H, bam_decode_norm_pages(Lmax)], caller-owned) receives, for page p of
+ * (b, h), max |k_j|_2 over keys j in 64 p .. 64 p + 63 below Lmax, computed in float32 and
+ * rounded up so that it is never below the exact norm.  k_cache: [B, H, Lmax, Dh] of
+ * in_dtype (BAM_BF16; Dh in {32, 64, 128}), 16-byte aligned.  The array is kept beside
+ * the cache: after keys of a page change, recompute it (this call recomputes every page)
+ * before the next skipping decode; pages at or beyond kv_len are never read.
+ */
+int bam_decode_norm_pages(int Lmax);
+bam_status bam_decode_key_norms(const void* k_cache, int in_dtype, int B, int H, int Lmax, int Dh, float* norms,
+                                void* stream);
+
+/*
+ * bam_attn_decode_skip - bam_attn_decode that leaves out the key ranges whose weights are
+ * zero in float32 ("Bayesian Attention Mechanism", "Highlights": retrieval far beyond the
+ * training context, where a prior that decays with distance gives far keys no weight).
+ * Arguments, flags, workspace and results are those of bam_attn_decode, plus key_norms
+ * from bam_decode_key_norms for the same cache (required; BAM_EINVAL if NULL).
+ * A first kernel takes the largest logit among the last 256 keys of each sequence, less a
+ * rounding margin, as a lower bound M- of its largest logit.  Each key range (split) then
+ * bounds its own logits from above, key by key, by c (b(i - j) + |q| |k|_page / sqrt(Dh))
+ * (log2 units) and, when that bound is more than 160 below M-, stores the partial of a
+ * range with no visible key instead of reading its K and V.  The full computation merges
+ * such a range with weight 2^(m_s - M) < 2^-160, which is 0 in float32, so the outputs
+ * are bit-for-bit those of bam_attn_decode on the same workspace layout.  The bounds
+ * assume finite q, k and table entries; with key norms that no longer bound the cache
+ * (stale after the cache changed) the result is undefined.
+ */
+bam_status bam_attn_decode_skip(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                                const int32_t* kv_len, int B, int H, int Lmax, int Dh,
+                                const float* alpha, const float* beta, const float* mu, const float* s,
+                                unsigned flags, const float* key_norms, void* o, int o_dtype, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bam_attn_decode_static - bam_attn_decode with no workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  It allocates nothing and calls no allocating routine:

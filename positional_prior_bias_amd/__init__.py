@@ -44,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "bam_fwd_workspace_size", "bam_attn_fwd", "bam_fwd_skip_plan_offset",
     "bam_decode_workspace_size", "bam_attn_decode", "bam_attn_decode_paged",
     "bam_decode_static_max_bytes", "bam_attn_decode_static",
+    "bam_decode_partials_layout", "bam_decode_norm_pages", "bam_decode_key_norms", "bam_attn_decode_skip",
     "bam_bwd_workspace_size", "bam_attn_bwd", "bam_attn_bwd_ex",
 )
 
@@ -83,6 +84,15 @@ def _declare(L):
     L.bam_decode_static_max_bytes.argtypes = []
     L.bam_attn_decode_static.restype = i
     L.bam_attn_decode_static.argtypes = [vp, vp, vp, i, vp, i, i, i, i, fp, fp, fp, fp, u, vp, i, fp, vp]
+    L.bam_decode_partials_layout.restype = i
+    L.bam_decode_partials_layout.argtypes = [i, i, i, i, ctypes.POINTER(sz), ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.bam_decode_norm_pages.restype = i
+    L.bam_decode_norm_pages.argtypes = [i]
+    L.bam_decode_key_norms.restype = i
+    L.bam_decode_key_norms.argtypes = [vp, i, i, i, i, i, fp, vp]
+    L.bam_attn_decode_skip.restype = i
+    L.bam_attn_decode_skip.argtypes = [vp, vp, vp, i, vp, i, i, i, i, fp, fp, fp, fp, u, fp, vp, i, fp, vp, sz,
+                                       vp]
     L.bam_bwd_workspace_size.restype = sz
     L.bam_bwd_workspace_size.argtypes = [i, i, i, i, u]
     L.bam_attn_bwd.restype = i
@@ -366,6 +376,67 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
                     o=None, lse=None, workspace=None, stream=None, table_ready=False, prior_ref=False,
                  prior=None):
     """Decode; q [B, H, Dh], caches [B, H, Lmax, Dh], kv_len int32 [B].  Returns (o, lse)."""
+    return _decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax, o_dtype, o, lse, workspace, stream,
+                   table_ready, prior_ref, prior, None)
+
+
+def bam_attn_decode_skip(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, key_norms=None, ssmax=True,
+                         o_dtype=None, o=None, lse=None, workspace=None, stream=None, table_ready=False,
+                         prior_ref=False, prior=None):
+    """bam_attn_decode that leaves out the key ranges whose weights are zero in float32;
+    key_norms [B, H, bam_decode_norm_pages(Lmax)] float32 from bam_decode_key_norms on the
+    same cache.  Same results, bit for bit."""
+    if key_norms is None:
+        raise BamError("key_norms is required (bam_decode_key_norms of the cache)")
+    return _decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax, o_dtype, o, lse, workspace, stream,
+                   table_ready, prior_ref, prior, key_norms)
+
+
+def bam_decode_norm_pages(Lmax) -> int:
+    return int(lib().bam_decode_norm_pages(Lmax))
+
+
+def bam_decode_key_norms(k_cache, norms=None, stream=None):
+    """Per-page (64 keys) maxima of the key norms of a cache [B, H, Lmax, Dh]: the float32
+    array [B, H, bam_decode_norm_pages(Lmax)] that bam_attn_decode_skip reads."""
+    torch = _torch()
+    B, H, Lmax, Dh = _shape(k_cache, "k_cache", 4)
+    npages = bam_decode_norm_pages(Lmax)
+    dev = k_cache.device
+    if norms is None:
+        norms = torch.empty((B, H, npages), dtype=torch.float32, device=dev)
+    else:
+        _expect(norms, "norms", shape=(B, H, npages), dtypes=(torch.float32,), device=dev)
+    st = lib().bam_decode_key_norms(_dev(k_cache, "k_cache"), _dtype_code(k_cache), B, H, Lmax, Dh,
+                                    _dev(norms, "norms"), _stream(stream))
+    _check(st, "bam_decode_key_norms")
+    return norms
+
+
+def bam_decode_partials_layout(B, H, Lmax, Dh):
+    """(byte offset, nsplit, chunk) of the per-range partials a decode call leaves in its
+    workspace: float32 records [B, H, nsplit, Dh + 2] = (m, l, o)."""
+    off, ns, ch = ctypes.c_size_t(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().bam_decode_partials_layout(B, H, Lmax, Dh, ctypes.byref(off), ctypes.byref(ns), ctypes.byref(ch)),
+           "bam_decode_partials_layout")
+    return int(off.value), int(ns.value), int(ch.value)
+
+
+def decode_skipped_fraction(workspace, kv_len, B, H, Lmax, Dh):
+    """Fraction of the key ranges holding visible keys whose partial the last decode call on
+    `workspace` left empty (m = -inf): for bam_attn_decode_skip, the ranges it skipped."""
+    torch = _torch()
+    off, ns, ch = bam_decode_partials_layout(B, H, Lmax, Dh)
+    part = workspace[off:off + 4 * B * H * ns * (Dh + 2)].view(torch.float32).view(B, H, ns, Dh + 2)
+    m = part[..., 0].cpu()
+    L = kv_len.cpu().long().clamp(1, Lmax)
+    live = (torch.arange(ns)[None, :] * ch < L[:, None])[:, None, :].expand(B, H, ns)
+    empty = torch.isneginf(m) & live
+    return float(empty.sum().item()) / float(live.sum().item())
+
+
+def _decode(q, k_cache, v_cache, kv_len, alpha, beta, mu, s, ssmax, o_dtype, o, lse, workspace, stream, table_ready,
+            prior_ref, prior, key_norms):
     torch = _torch()
     B, H, Lmax, Dh = _shape(k_cache, "k_cache", 4)
     flags = _flags(False, ssmax, prior_ref, prior) | (BAM_TABLE_READY if table_ready else 0)
@@ -391,10 +462,19 @@ def bam_attn_decode(q, k_cache, v_cache, kv_len, alpha, beta, mu=None, s=None, s
     nb = bam_decode_workspace_size(B, H, Lmax, Dh)
     ws = _workspace(nb, dev, workspace)
     a, b_, m_, s_ = _param_ptrs(alpha, beta, mu, s)
-    st = lib().bam_attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), in_code,
-                               _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
-                               _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "bam_attn_decode")
+    if key_norms is None:
+        st = lib().bam_attn_decode(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), in_code,
+                                   _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags, _dev(o, "o"), oc,
+                                   _dev(lse, "lse"), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+        _check(st, "bam_attn_decode")
+    else:
+        _expect(key_norms, "key_norms", shape=(B, H, bam_decode_norm_pages(Lmax)), dtypes=(torch.float32,),
+                device=dev)
+        st = lib().bam_attn_decode_skip(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), in_code,
+                                        _dev(kv_len, "kv_len"), B, H, Lmax, Dh, a, b_, m_, s_, flags,
+                                        _dev(key_norms, "key_norms"), _dev(o, "o"), oc, _dev(lse, "lse"), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream))
+        _check(st, "bam_attn_decode_skip")
     return o, lse
 
 

@@ -226,10 +226,12 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
 // ---------------------------------------------------------------------------------------
 namespace {
 struct DecodeLayout {
-  size_t tab_off, part_off, total;
+  size_t tab_off, part_off, bound_off, total;
   int tab_stride, nsplit, chunk;
 };
 
+// workspace: the distance table, the split partials, then two floats per (b, h) for the
+// skipping bound
 DecodeLayout decode_layout(int B, int H, int Lmax, int Dh) {
   DecodeLayout d;
   d.tab_stride = pad64(Lmax);
@@ -237,7 +239,8 @@ DecodeLayout decode_layout(int B, int H, int Lmax, int Dh) {
   d.nsplit = (Lmax + d.chunk - 1) / d.chunk;
   d.tab_off = 0;
   d.part_off = align_up((size_t)H * d.tab_stride * sizeof(float));
-  d.total = d.part_off + align_up((size_t)B * H * d.nsplit * (Dh + 2) * sizeof(float));
+  d.bound_off = d.part_off + align_up((size_t)B * H * d.nsplit * (Dh + 2) * sizeof(float));
+  d.total = d.bound_off + align_up((size_t)B * H * 2 * sizeof(float));
   return d;
 }
 }  // namespace
@@ -252,7 +255,7 @@ bam_status decode_common(const void* q, const void* k, const void* v, int in_dty
                          int max_blocks, int num_pages, int page_size, const int32_t* kv_len, int B, int H,
                          int Lmax, int Dh, const float* alpha, const float* beta, const float* mu,
                          const float* s, unsigned flags, void* o, int o_dtype, float* lse, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, const float* key_norms = nullptr) {
   if (!dims_ok(B, H, Lmax) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       lse == nullptr || kv_len == nullptr || workspace == nullptr || !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
@@ -290,6 +293,9 @@ bam_status decode_common(const void* q, const void* k, const void* v, int in_dty
   a.o = o;
   a.o_f32 = o_dtype == BAM_F32;
   a.lse = lse;
+  a.key_norms = key_norms;
+  a.npages = (Lmax + bam::kNormPage - 1) / bam::kNormPage;
+  a.bound = (float*)((char*)workspace + L.bound_off);
   return hip_status(bam::launch_decode(a, Dh, st));
 }
 }  // namespace
@@ -301,6 +307,35 @@ bam_status bam_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            void* stream) {
   return decode_common(q, k_cache, v_cache, in_dtype, nullptr, 0, 0, 0, kv_len, B, H, Lmax, Dh, alpha, beta, mu, s,
                        flags, o, o_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+bam_status bam_decode_partials_layout(int B, int H, int Lmax, int Dh, size_t* offset, int* nsplit, int* chunk) {
+  if (offset == nullptr || nsplit == nullptr || chunk == nullptr || bam_decode_workspace_size(B, H, Lmax, Dh) == 0)
+    return BAM_EINVAL;
+  const DecodeLayout L = decode_layout(B, H, Lmax, Dh);
+  *offset = L.part_off;
+  *nsplit = L.nsplit;
+  *chunk = L.chunk;
+  return BAM_OK;
+}
+
+int bam_decode_norm_pages(int Lmax) { return Lmax <= 0 ? 0 : (Lmax + bam::kNormPage - 1) / bam::kNormPage; }
+
+bam_status bam_decode_key_norms(const void* k_cache, int in_dtype, int B, int H, int Lmax, int Dh, float* norms,
+                                void* stream) {
+  if (!dims_ok(B, H, Lmax) || !aligned16(k_cache) || norms == nullptr) return BAM_EINVAL;
+  if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64 && Dh != 128)) return BAM_EUNSUPPORTED;
+  return hip_status(bam::launch_decode_key_norms(k_cache, B, H, Lmax, Dh, norms, (hipStream_t)stream));
+}
+
+bam_status bam_attn_decode_skip(const void* q, const void* k_cache, const void* v_cache, int in_dtype,
+                                const int32_t* kv_len, int B, int H, int Lmax, int Dh, const float* alpha,
+                                const float* beta, const float* mu, const float* s, unsigned flags,
+                                const float* key_norms, void* o, int o_dtype, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (key_norms == nullptr) return BAM_EINVAL;
+  return decode_common(q, k_cache, v_cache, in_dtype, nullptr, 0, 0, 0, kv_len, B, H, Lmax, Dh, alpha, beta, mu, s,
+                       flags, o, o_dtype, lse, workspace, workspace_bytes, stream, key_norms);
 }
 
 // ---------------------------------------------------------------------------------------

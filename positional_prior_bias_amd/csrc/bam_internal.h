@@ -95,10 +95,19 @@ struct DecodeArgs {
   void* o;
   bool o_f32;
   float* lse;
+  // prior-aware skipping (contiguous caches): key_norms [B,H,npages] per-64-key-page
+  // maxima of |k|, or null (no skipping); bound [B,H,2] written by the bound kernel (a
+  // lower bound of each row's largest logit, and |q| log2(e) / sqrt(Dh) rounded up)
+  const float* key_norms;
+  int npages;
+  float* bound;
 };
 
 int decode_chunk_keys(int Lmax, int Dh, int BH);
 hipError_t launch_decode(const DecodeArgs& a, int Dh, hipStream_t stream);
+constexpr int kNormPage = 64;   // keys per page of the key-norm maxima
+hipError_t launch_decode_key_norms(const void* k, int B, int H, int Lmax, int Dh, float* norms,
+                                   hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

@@ -23,6 +23,14 @@
 // page_size is a multiple of 64, so a wave tile never straddles two pages and costs one
 // scalar table read; page ids are clamped to [0, num_pages) so a bad table cannot read
 // outside the pages.
+// Prior-aware skipping (SKIP, contiguous caches): a bound kernel first takes, per (b, h),
+// the largest logit of the last 256 keys (minus a rounding margin) as a lower bound M- of
+// the row's largest logit.  Each range then bounds its own logits from above, key by key,
+// by c (b(d) + |q| |k|_page / sqrt(Dh)) with the caller's per-page maxima of |k|, and a
+// range whose bound sits more than 160 (log2 units) below M- writes the partial of a range
+// with no visible key (m = -inf, l = 0, o = 0) without reading its K and V.  In the full
+// computation that range's merge weight 2^(m_s - M) is below 2^-160, i.e. exactly 0 in
+// float32, so both give the same bits.
 #include <float.h>
 
 #include "bam_device.h"
@@ -54,10 +62,11 @@ __device__ __forceinline__ float dot8(const float* q, const u32x4& w) {
   return acc;
 }
 
-template <int DH, bool PAGED>
+template <int DH, bool PAGED, bool SKIP>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   using S = DecodeShape<DH>;
   constexpr int LPK = S::LPK, KPI = S::KPI, KT = S::KT;
+  static_assert(!(PAGED && SKIP), "skipping is for contiguous caches");
   __shared__ float red[kWaves][DH + 2];
 
   const int sidx = blockIdx.x;
@@ -97,6 +106,34 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   float o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+  if constexpr (SKIP) {
+    // upper bound of this range's logits: c (b(i - j) + |q| |k|_page(j) / sqrt(Dh)), in
+    // log2 units, over its keys; every thread takes every 256th key
+    const float qn = a.bound[2 * bh + 1];
+    const float* __restrict__ nrm = a.key_norms + (size_t)bh * a.npages;
+    float ub = kNegInf;
+    for (int key = kbeg + tid; key < kend; key += 256)
+      ub = fmaxf(ub, fmaf(tabh[iq - key], kLog2e, qn * nrm[key / kNormPage]));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) ub = fmaxf(ub, __shfl_xor(ub, off, 64));
+    if (lane == 0) red[wave][0] = ub;
+    __syncthreads();
+    ub = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+    ub = C * ub;
+    if (ub != kNegInf) ub += fabsf(ub) * 0x1p-10f + 1.0f;   // covers the rounding of the logits
+    const bool skip = ub < a.bound[2 * bh] - 160.0f;
+    __syncthreads();                                   // red is reused below
+    if (skip) {
+      float* part = a.part + ((size_t)bh * a.nsplit + sidx) * (DH + 2);
+      if (tid < DH) part[2 + tid] = 0.f;
+      if (tid == 0) {
+        part[0] = kNegInf;
+        part[1] = 0.f;
+      }
+      return;
+    }
+  }
 
   for (int tb = kbeg + wave * KT; tb < kend; tb += kWaves * KT) {
     // rows of this tile: Kt / Vt + (tile-relative key) * DH
@@ -192,6 +229,94 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// Per (b, h): M- = the largest logit of the last min(n, 256) keys, computed as the split
+// kernel computes logits (the same scaled query, the same table entry, a different
+// summation order) and lowered by a margin that covers the difference, so M- never exceeds
+// the largest logit the split kernel finds; and |q| log2(e) / sqrt(Dh), rounded up.
+template <int DH>
+__global__ void __launch_bounds__(256) decode_bound_kernel(DecodeArgs a) {
+  __shared__ float smax[4];
+  __shared__ float sq;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int L = a.kv_len[b];
+  L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);
+  const int iq = L - 1;
+  const float qscale = kLog2e / __builtin_sqrtf((float)DH);
+  const uint16_t* __restrict__ qp = (const uint16_t*)a.q + (size_t)bh * DH;
+  if (tid == 0) {
+    float ss = 0.f;
+    for (int e = 0; e < DH; e += 2) {
+      const uint32_t w = *(const uint32_t*)(qp + e);
+      const float x0 = bf16_lo(w) * qscale, x1 = bf16_hi(w) * qscale;
+      ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+    }
+    // the sum of DH squares rounds by at most DH 2^-24 of itself, the root by half that
+    sq = __builtin_sqrtf(ss) * (1.0f + 0x1p-14f);
+  }
+  const float c = ssmax_c(a.ssmax, a.ssmax ? a.s[h] : 1.0f, L);
+  const float C = fmaxf(c, FLT_MIN);
+  const float* __restrict__ tabh = a.tab + (size_t)h * a.tab_stride;
+  float t = kNegInf;
+  const int key = iq - tid;
+  if (key >= 0) {
+    const uint16_t* __restrict__ kp = (const uint16_t*)a.k + ((size_t)bh * a.Lmax + key) * DH;
+    float d = 0.f;
+    for (int e = 0; e < DH; e += 8) {
+      const u32x4 w = *(const u32x4*)(kp + e);
+      const u32x4 qw = *(const u32x4*)(qp + e);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        d = fmaf(bf16_lo(qw[x]) * qscale, bf16_lo(w[x]), d);
+        d = fmaf(bf16_hi(qw[x]) * qscale, bf16_hi(w[x]), d);
+      }
+    }
+    t = C * fmaf(tabh[iq - key], kLog2e, d);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) t = fmaxf(t, __shfl_xor(t, off, 64));
+  if (lane == 0) smax[wave] = t;
+  __syncthreads();
+  if (tid == 0) {
+    float mx = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+    // two fp32 dot products of the same terms in different orders differ by at most about
+    // DH 2^-23 of the sum of |terms|; the margin is far wider, and -inf stays -inf
+    mx -= fabsf(mx) * 0x1p-10f + 1.0f;
+    a.bound[2 * bh] = mx;
+    a.bound[2 * bh + 1] = sq;
+  }
+}
+
+// Per-page maxima of the key norms: norms[b][h][p] = max |k_j| over keys j of page p
+// (kNormPage keys; keys at or beyond Lmax count as zero), computed in fp32 and rounded up
+// so that it bounds the exact norm.  One wave per page, one lane per key.
+template <int DH>
+__global__ void __launch_bounds__(256) decode_key_norms_kernel(const uint16_t* __restrict__ k, int H, int Lmax,
+                                                               int npages, float* __restrict__ norms) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int page = blockIdx.x * 4 + wave;
+  const int bh = blockIdx.y;
+  if (page >= npages) return;
+  const int key = page * kNormPage + lane;
+  float ss = 0.f;
+  if (key < Lmax) {
+    const uint16_t* __restrict__ kp = k + ((size_t)bh * Lmax + key) * DH;
+    for (int e = 0; e < DH; e += 8) {
+      const u32x4 w = *(const u32x4*)(kp + e);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float x0 = bf16_lo(w[x]), x1 = bf16_hi(w[x]);
+        ss = fmaf(x0, x0, fmaf(x1, x1, ss));
+      }
+    }
+  }
+  float n = __builtin_sqrtf(ss) * (1.0f + 0x1p-14f);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) n = fmaxf(n, __shfl_xor(n, off, 64));
+  if (lane == 0) norms[(size_t)bh * npages + page] = n;
+}
+
 // Merge the per-range partials of one (b, h): M = max m_s, L = sum 2^(m_s - M) l_s,
 // O = sum 2^(m_s - M) o_s / L.  Four waves take every fourth range (independent loads,
 // unrolled), then combine through LDS.
@@ -245,10 +370,16 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
 
 template <int DH>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.block_table)
-    hipLaunchKernelGGL((decode_split_kernel<DH, true>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<DH, false>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  if (a.block_table) {
+    hipLaunchKernelGGL((decode_split_kernel<DH, true, false>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  } else if (a.key_norms) {
+    hipLaunchKernelGGL(decode_bound_kernel<DH>, dim3(a.B * a.H), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_split_kernel<DH, false, true>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<DH, false, false>), dim3(a.nsplit, a.H, a.B), dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3(a.B * a.H), dim3(256), 0, stream, a);
@@ -270,6 +401,20 @@ int decode_chunk_keys(int Lmax, int Dh, int BH) {
   if (want > 2048) want = 2048;
   if (want < tile) want = tile;
   return ((want + tile - 1) / tile) * tile;
+}
+
+hipError_t launch_decode_key_norms(const void* k, int B, int H, int Lmax, int Dh, float* norms,
+                                   hipStream_t stream) {
+  const int npages = (Lmax + kNormPage - 1) / kNormPage;
+  const dim3 grid((npages + 3) / 4, B * H);
+  const uint16_t* kp = (const uint16_t*)k;
+  switch (Dh) {
+    case 32: hipLaunchKernelGGL(decode_key_norms_kernel<32>, grid, dim3(256), 0, stream, kp, H, Lmax, npages, norms); break;
+    case 64: hipLaunchKernelGGL(decode_key_norms_kernel<64>, grid, dim3(256), 0, stream, kp, H, Lmax, npages, norms); break;
+    case 128: hipLaunchKernelGGL(decode_key_norms_kernel<128>, grid, dim3(256), 0, stream, kp, H, Lmax, npages, norms); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int Dh, hipStream_t stream) {

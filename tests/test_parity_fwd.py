@@ -166,3 +166,34 @@ def test_long_prefill_sampled_rows():
         worst_l = max(worst_l, max_abs(lh[0, h, rows], L))
     within(worst_o, BF16_O_ABS, f"T = 32768 O over {rows.size} rows per head")
     within(worst_l, BF16_LSE_ABS, f"T = 32768 lse over {rows.size} rows per head")
+
+
+def test_prefill_131072_sampled_rows():
+    """B=1, H=12, T=131072, the length sweep's inputs (Q, K, V drawn on the GPU from seed 3,
+    the 32,768-token prefill's heads): per head the first and last 64 rows, every 8192-row
+    boundary +-1 and 64 random rows, against the oracle on the same bf16 values."""
+    torch = torch_mod()
+    T = 131072
+    w = wl.long_prefill_device(T=T, B=1)
+    p = params(w)
+    o, lse = _bam().bam_attn_fwd(w.q, w.k, w.v, p["alpha"], p["beta"], p["mu"], p["s"], causal=True, ssmax=True,
+                                 o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(131072)
+    rows = set(range(64)) | set(range(T - 64, T))
+    for b in range(8192, T, 8192):
+        rows |= {b - 1, b, b + 1}
+    rows |= set(rng.integers(0, T, 64).tolist())
+    rows = np.array(sorted(rows))
+    ridx = torch.from_numpy(rows).cuda()
+    oh = host(o[0].index_select(1, ridx))
+    lh = host(lse[0].index_select(1, ridx))
+    worst_o = worst_l = 0.0
+    for h in range(w.H):
+        qh, kh, vh = (host(x[0, h]) for x in (w.q, w.k, w.v))
+        O, L = oracle.attn_fwd_rows(qh, kh, vh, rows, w.alpha[h], w.beta[h], w.mu[h], w.s[h], causal=True,
+                                    ssmax=True, chunk=64)
+        worst_o = max(worst_o, max_abs(oh[h], O))
+        worst_l = max(worst_l, max_abs(lh[h], L))
+    within(worst_o, BF16_O_ABS, f"T = 131072 O over {rows.size} rows per head")
+    within(worst_l, BF16_LSE_ABS, f"T = 131072 lse over {rows.size} rows per head")
