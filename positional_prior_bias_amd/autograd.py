@@ -66,15 +66,39 @@ def _alibi_slopes(n_heads):
     return [2.0 ** (-8.0 * (h + 1) / n_heads) for h in range(n_heads)]
 
 
+# Initial values of the per-head prior parameters by option name, as the pages'
+# AttentionPrior module offers them ("Bayesian Attention Mechanism" README, "Implementation
+# Details"); a number instead of a name starts every head at that number.
+#
+#   parameter     option     initial value of head h (H heads)
+#   theta_alpha   "slope"    2^(-8 (h + 1) / H), the ALiBi slopes
+#   theta_alpha   "sampled"  exp(z_h), z_h standard normal
+#   theta_beta    "linear"   h / (H - 1), evenly from 0 to 1
+#   theta_beta    "sampled"  z_h, standard normal
+#   theta_beta    (not trained)  1
+#   theta_mu      a number only
+_NAMED_INIT = {
+    ("theta_alpha", "slope"): lambda H, gen: torch.tensor(_alibi_slopes(H), dtype=torch.float32),
+    ("theta_alpha", "sampled"): lambda H, gen: torch.randn(H, generator=gen, dtype=torch.float32).exp(),
+    ("theta_beta", "linear"): lambda H, gen: torch.linspace(0, 1, H, dtype=torch.float32),
+    ("theta_beta", "sampled"): lambda H, gen: torch.randn(H, generator=gen, dtype=torch.float32),
+}
+
+
+def _initial(name, option, H, generator, device):
+    if isinstance(option, str):
+        if (name, option) not in _NAMED_INIT:
+            raise ValueError(f"{name}: unknown initialisation {option!r}")
+        return _NAMED_INIT[(name, option)](H, generator).to(device)
+    return torch.full((H,), float(option), dtype=torch.float32, device=device)
+
+
 class BamAttention(torch.nn.Module):
     """Causal attention with a trained BAM prior and SSMax, on the HIP kernels.
 
-    Initialisation options follow the pages' AttentionPrior module:
-      theta_alpha_init: "slope" (the ALiBi slopes), "sampled" (exp of a standard normal)
-        or a number;
-      theta_beta_init: "linear" (linspace(0, 1) over the heads), "sampled" (standard
-        normal) or a number; with train_theta_beta=False theta_beta is fixed at 1;
-      theta_mu_init: a number (0 by default), trained only with train_theta_mu=True.
+    Initialisation options (the table above _NAMED_INIT): theta_alpha_init "slope",
+    "sampled" or a number; theta_beta_init "linear", "sampled" or a number (fixed at 1 when
+    train_theta_beta is False); theta_mu_init a number, trained only with train_theta_mu.
     s (SSMax strength, one per head) starts at 1 / ln(max_seq_len), so the SSMax factor
     s ln(n) is 1 at the training context length; the pages give no initial value.
     """
@@ -84,22 +108,10 @@ class BamAttention(torch.nn.Module):
                  ssmax=True, train_s=True, device=None, generator=None):
         super().__init__()
         H = n_heads
-        f32 = dict(dtype=torch.float32, device=device)
-        if theta_alpha_init == "slope":
-            ta = torch.tensor(_alibi_slopes(H), **f32)
-        elif theta_alpha_init == "sampled":
-            ta = torch.randn(H, generator=generator, dtype=torch.float32).exp().to(device)
-        else:
-            ta = torch.full((H,), float(theta_alpha_init), **f32)
-        if train_theta_beta and theta_beta_init == "linear":
-            tb = torch.linspace(0, 1, H, **f32)
-        elif train_theta_beta and theta_beta_init == "sampled":
-            tb = torch.randn(H, generator=generator, dtype=torch.float32).to(device)
-        elif train_theta_beta:
-            tb = torch.full((H,), float(theta_beta_init), **f32)
-        else:
-            tb = torch.ones(H, **f32)
-        tm = torch.full((H,), float(theta_mu_init), **f32)
+        f32 = dict(dtype=torch.float32, device=device)   # for s below
+        ta = _initial("theta_alpha", theta_alpha_init, H, generator, device)
+        tb = _initial("theta_beta", theta_beta_init if train_theta_beta else 1.0, H, generator, device)
+        tm = _initial("theta_mu", float(theta_mu_init), H, generator, device)
         self.theta_alpha = torch.nn.Parameter(ta, requires_grad=train_theta_alpha)
         self.theta_beta = torch.nn.Parameter(tb, requires_grad=train_theta_beta)
         self.theta_mu = torch.nn.Parameter(tm, requires_grad=train_theta_mu)
