@@ -5,8 +5,8 @@
 
 Prints ONE JSON line.  `value` is the training-shape causal forward (B=32, H=12,
 T=512, Dh=64, bf16 in / bf16 out, fp32 accumulate, SSMax on) in TFLOP/s, with one
-step = one bam_attn_fwd call (distance table + attention kernel) on inputs already
-resident in HBM.  `parts` carries the other figures the metric names: the forward at
+step = one bam_attn_fwd call (at this shape one kernel, which computes its own bias)
+on inputs already resident in HBM.  `parts` carries the other figures the metric names: the forward at
 T=32768 (% of bf16 MFMA peak), decode against a 256,000-token KV cache (GB/s, % of
 HBM peak) and the training-shape forward+backward.  FLOPs count 4*Dh per visible
 causal (query, key) pair for the forward and 10*Dh for the backward; decode bytes are

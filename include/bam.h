@@ -167,6 +167,11 @@ bam_status bam_prior_table_ex(const float* alpha, const float* beta, const float
  * Supported: in_dtype BAM_BF16 with Dh in {32, 64, 128} (bf16 MFMA, fp32 accumulate) and
  * T * Dh * 2 < 2^31 bytes per (b, h); in_dtype BAM_F32 with Dh in {32, 64} (fp32
  * throughout).  Larger requests return BAM_EUNSUPPORTED.  BAM_SKIP_FAR: see above.
+ * Bias: for in_dtype BAM_BF16, Dh = 64, T <= 512 and the alpha or reference prior, the
+ * kernel computes the bias of each distance itself in float32 arithmetic (within a few
+ * float32 ulps of the distance table's value, which is derived in float64) and builds no
+ * table unless BAM_SKIP_FAR needs one; BAM_TABLE_READY then changes nothing.  Every other
+ * case reads the distance table from the workspace.
  */
 size_t bam_fwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
 bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtype,

@@ -173,7 +173,10 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   hipStream_t st = (hipStream_t)stream;
   float* tab = (float*)workspace;
   hipError_t e = hipSuccess;
-  if (!(flags & BAM_TABLE_READY)) {
+  // Up to kFwdStripT the short-sequence Dh = 64 kernel computes the alpha and reference
+  // priors' bias itself; the table is then built only for the skipping plan, which reads it.
+  const bool inkernel = bf16 && Dh == 64 && T <= bam::kFwdStripT && kind != bam::kPriorSandwich;
+  if (!(flags & BAM_TABLE_READY) && (!inkernel || (flags & BAM_SKIP_FAR))) {
     if (bf16)
       e = bam::launch_prior_table_ex(alpha, beta, mu, kind, H, g.d0, -1, g.n, g.stride, causal ? 0 : -(T - 1), T - 1,
                                      std::sqrt((float)Dh), tab, nullptr, nullptr, nullptr, st);
@@ -199,6 +202,13 @@ bam_status bam_attn_fwd(const void* q, const void* k, const void* v, int in_dtyp
   a.o_f32 = o_dtype == BAM_F32;
   a.lse = lse;
   a.first_tile = nullptr;
+  a.bias_inkernel = inkernel;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.mu = mu;
+  a.kind = kind;
+  a.dlo = causal ? 0 : -(T - 1);
+  a.dhi = T - 1;
   if (flags & BAM_SKIP_FAR) {
     const FwdLayout L = fwd_layout(B, H, T, Dh, flags);
     char* ws = (char*)workspace;

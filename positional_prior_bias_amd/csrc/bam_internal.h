@@ -44,6 +44,14 @@ struct FwdArgs {
   bool o_f32;
   float* lse;
   const int32_t* first_tile;   // per work-group first key tile (prior-aware skipping), or null
+  // The short-sequence Dh = 64 kernel computes its bias window itself (bias_inkernel, for
+  // T <= kFwdStripT and the alpha and reference priors): the head's parameters, the prior
+  // kind and the visible distance range [dlo, dhi]; the table is then not read.
+  bool bias_inkernel;
+  const float* alpha;
+  const float* beta;
+  const float* mu;
+  int kind, dlo, dhi;
 };
 
 // Query rows per work-group of the bf16 forward kernel: two 32-row blocks per wave (256
@@ -51,6 +59,9 @@ struct FwdArgs {
 // Short sequences have few key tiles per work-group, so finer work-groups balance the
 // causal triangle better than the operand reuse of two blocks per wave pays.
 constexpr int kFwdShortT = 1024;
+// Up to this length the short-sequence Dh = 64 kernel computes the alpha and reference
+// priors' bias itself (one strip of window entries per work-group, in LDS).
+constexpr int kFwdStripT = 512;
 constexpr int fwd_bf16_rows_per_block(int Dh, int T) {
   return (Dh == 128 || (Dh == 64 && T <= kFwdShortT)) ? 128 : 256;
 }

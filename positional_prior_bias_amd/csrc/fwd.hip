@@ -39,6 +39,7 @@
 
 #include "bam_device.h"
 #include "bam_internal.h"
+#include "prior_eval.h"
 
 namespace bam {
 
@@ -79,6 +80,16 @@ constexpr int kRingEntries = 384;
 constexpr int kRingStride = 400;
 static_assert(kRingStride >= kRingEntries && kRingStride % 32 == 16, "ring copies overlap or share banks");
 
+// The strip: with the bias computed in the kernel (bias_inkernel, T <= kFwdStripT), the
+// work-group computes every window entry of all its tiles once, before its first tile:
+// 64 (ntiles + 2) <= kStripEntries consecutive entries per copy, so tile t's window is the
+// 192 entries from 64 t.  It shares the ring's LDS (whichever the launch uses); copies
+// kStripStride floats apart (656 = 20 * 32 + 16) for the same bank spread.  The
+// work-group's LDS grows to 38,016 bytes (38,400 allocated): four still fit in a CU.
+constexpr int kStripEntries = 64 * (kFwdStripT / kNK + 2);
+constexpr int kStripStride = 656;
+static_assert(kStripStride >= kStripEntries && kStripStride % 32 == 16, "strip copies overlap or share banks");
+
 // bf16 forward.  NQB = query blocks of 32 rows per wave (2 for Dh <= 64: the K and V^T
 // operand reads from LDS are shared by both blocks; 1 for Dh = 128 to bound registers).
 // SKIP: the launch carries a prior-aware skipping plan (causal only); a separate
@@ -116,7 +127,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   typedef typename std::conditional<RING, uint32_t[4], Tile>::type ThirdTile;   // unused with the ring
   __shared__ __attribute__((aligned(16))) ThirdTile tCst;
   Tile& tC = *reinterpret_cast<Tile*>(&tCst);
-  __shared__ __attribute__((aligned(16))) float wring[RING ? NCOPY * kRingStride : 4];
+  __shared__ __attribute__((aligned(16))) float wring[RING ? NCOPY * kStripStride : 4];   // ring or strip
 
   const int BH = a.B * a.H;
   // Work-group i runs on XCD i % 8 (one L2 each).  With B * H a multiple of 8 every query
@@ -227,6 +238,22 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     const int pos = (mirror && slot < 2) ? 256 + 64 * slot : 64 * slot;
     lds_dma4(rW, issue_lane() * 4, (u0 + cpy + 64 * k) * 4, &wring[cpy * kRingStride + pos]);
   };
+  // The strip (bias_inkernel): entry x of copy c is table entry u0 + c + x, u0 that of
+  // tile 0, that is sqrt(Dh) times the bias at distance tab_d0 - u0 - c - x, computed in
+  // float32 (prior_bias_f32: within a few ulps of the table's float64-derived value).
+  // Thread l computes table entries u0 + l, u0 + l + 256, ... once and stores each in both
+  // copies.  That takes the distance-table launch out of the forward call.
+  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters, loaded before the prologue's loads
+  auto fill_strip = [&]() {
+    const int u0 = a.tab_d0 - (i0 + MQ - 1 - jb);
+    const float sc = __builtin_sqrtf((float)DH);
+    for (int x = tid; x <= kStripEntries; x += 256) {
+      const int d = a.tab_d0 - (u0 + x);
+      const float b = (d >= a.dlo && d <= a.dhi) ? prior_bias_f32(a.kind, pa, pb, pm, d) * sc : kNegInf;
+      if (x < kStripEntries) wring[x] = b;
+      if (x >= 1) wring[kStripStride + x - 1] = b;
+    }
+  };
   // the segment tile t adds (k = 2): one load per wave (copy wave & 1, mirror wave >> 1)
   auto ring_next = [&](int t) { ring_load(t, 2, wave & 1, wave >> 1); };
 
@@ -289,7 +316,8 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
             sacc[qb2][kb][4 * g + 3] = v4[3];
           }
         } else {
-          const f32x2* __restrict__ wv = (const f32x2*)&wring[wcopy * kRingStride + 64 * (t & 3)];
+          const f32x2* __restrict__ wv = (const f32x2*)&wring[a.bias_inkernel ? wcopy * kStripStride + 64 * t
+                                                                               : wcopy * kRingStride + 64 * (t & 3)];
           const int y2 = ((ybase - wcopy) >> 1) + 16 * (kb - qb2);   // 8-byte units
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -439,9 +467,16 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   // registers defined there.
   // With the ring, tile 0's window (segments 0 .. 2 of both copies and the mirrors of slots
   // 0 and 1: ten loads, three per wave, the surplus repeating) goes first; each later tile's
-  // segment is issued one tile ahead, after the barrier that frees its slot.
+  // segment is issued one tile ahead, after the barrier that frees its slot.  The strip is
+  // computed while tile 0 and Q load.
+  if (RING && a.bias_inkernel) {
+    // loaded (and waited for) before any tile load is in flight
+    pa = a.alpha[h];
+    pb = a.beta[h];
+    pm = a.mu ? a.mu[h] : 0.f;
+  }
   BAM_WAIT_VMCNT(0);
-  if constexpr (RING) {
+  if (RING && !a.bias_inkernel) {
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       const int x = (wave * 3 + r) % 10;
@@ -463,6 +498,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       }
     }
   }
+  if (RING && a.bias_inkernel) fill_strip();
   if (!RING && ntiles > 1) {
     issue_tile(tB, jb + kNK);
     BAM_WAIT_VMCNT(LPT);       // tile 0 and Q landed (tile 1 may be in flight)
@@ -483,17 +519,18 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     // Two stages: tile t + 1 and its ring segment (whose slot held tile t - 1's first
     // segment) load while tile t is computed.  With three or more waves per SIMD, and the keys of a
     // short sequence mostly in L2, one tile of lead time is enough; it was 2% faster than
-    // three stages at T = 512 and halves the buffers.
+    // three stages at T = 512 and halves the buffers.  The strip needs no loads.
+    const bool ring = !a.bias_inkernel;
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) {
-        ring_next(t + 1);
+        if (ring) ring_next(t + 1);
         issue_tile(tB, jb + (t + 1) * kNK);
       }
       compute_tile(tA, t);
       advance();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) {
-        ring_next(t + 2);
+        if (ring) ring_next(t + 2);
         issue_tile(tA, jb + (t + 2) * kNK);
       }
       compute_tile(tB, t + 1);

@@ -6,7 +6,9 @@
 // n values per head replaces the dense T x T matrix; it is rebuilt on every call since
 // alpha and beta are trained parameters ("Bayesian Attention Mechanism",
 // "Implementation Details").  One power per (head, distance): the exponent in float64,
-// the final 2^fraction in float32 (pow_pos), rounded once to float32.
+// the final 2^fraction in float32 (pow_pos), rounded once to float32.  The value and
+// derivatives at one distance come from prior_bias_at, which the short-sequence forward
+// kernel also calls for its own bias window.
 //
 // The same table carries any other bias that depends on the head and i - j only.  The
 // Sandwich bias (attention-gym "Score Mods", "Sandwich") is the inner product of two
@@ -15,6 +17,7 @@
 #include "../../include/bam.h"
 #include "bam_device.h"
 #include "bam_internal.h"
+#include "prior_eval.h"
 
 namespace bam {
 
@@ -29,20 +32,6 @@ namespace bam {
 // violates the precondition of finite parameters and counts as no frequency, so every
 // entry is finite), and the derivative tables are zero.
 constexpr int kSandwichMaxFreq = 4096;
-
-// u^e for u > 0: the exponent y = e log2(u) in float64, split into an integer n and a
-// fraction f in [0, 1); 2^f in float32 (one v_exp_f32, about 1 ulp), scaled by 2^n
-// exactly.  The result is within about 2 float32 ulps of the float64 pow, which it
-// replaces because the table is rounded to float32 anyway and pow costs several times as
-// much.  log2(u) is returned for the derivative tables.  Exponents beyond +-1000 (the
-// value is then 0 or inf in float32) go through pow.
-__device__ __forceinline__ double pow_pos(double u, double e, double& l2) {
-  l2 = log2(u);
-  const double y = e * l2;
-  if (!(fabs(y) < 1000.0)) return pow(u, e);
-  const double n = floor(y);
-  return ldexp((double)exp2f((float)(y - n)), (int)n);
-}
 
 namespace {
 
@@ -85,51 +74,22 @@ __global__ void __launch_bounds__(256) prior_table_kernel(const float* __restric
   const double be = beta[h];
   const double m = mu ? (double)mu[h] : 0.0;
   const bool der = ta || tb || tm;   // derivative tables wanted (the forward's table is bias only)
-  double b, da = 0.0, db = 0.0, dm = 0.0;
+  double b;
+  PriorDerivs D;
   if (kind == kPriorSandwich) {
     double acc = 0.0;
     for (int i = 0; i < nf; ++i) acc += cos((double)d / inv_w[i]);
     b = acc / a;
-  } else if (kind == kPriorRef) {
-    // b = -e^ta g^tb, g = |x| + eps: db/dta = b, db/dtb = b ln g,
-    // db/dtm = -b tb sign(x) / g * (e^tm + e^-tm)
-    const double em = exp(m), emi = exp(-m);
-    const double x = -(double)d - (em - emi);
-    const double g = fabs(x) + (double)BAM_REF_EPS;
-    double l2g;
-    b = -exp(a) * pow_pos(g, be, l2g);
-    if (der) {
-      da = b;
-      db = b * l2g * 0.6931471805599453;   // b ln g
-      const double sg = x > 0.0 ? 1.0 : (x < 0.0 ? -1.0 : 0.0);
-      dm = -b * be * sg / g * (em + emi);
-    }
   } else {
-    const double x = (double)d - m;
-    const double u = __builtin_isinf(a) ? 0.0 : fabs(x) / a;
-    if (be == 0.0) {
-      b = -1.0;                                   // 0^0 = 1
-      if (u != 0.0) db = -log(u);
-    } else if (u == 0.0) {
-      b = be > 0.0 ? 0.0 : -__builtin_huge_val();  // beta < 0 at u = 0: precondition violated
-    } else {
-      double l2u;
-      const double p = pow_pos(u, be, l2u);
-      b = -p;
-      if (der) {
-        da = be * p / a;
-        db = -p * l2u * 0.6931471805599453;  // -p ln u
-        dm = be * p / x;                     // db/dmu, dx/dmu = -1
-      }
-    }
+    b = prior_bias_at(kind, a, be, m, d, der, D);
   }
   // The derivatives saturate at +-FLT_MAX: where u^beta overflows float32 the bias is -inf
   // and the weight exactly 0, and the backward's product 0 * derivative must stay 0.
   const double kFltMax = 3.4028234663852886e38;
   tab[idx] = (float)(b * scale);
-  if (ta) ta[idx] = (float)fmin(kFltMax, fmax(-kFltMax, da));
-  if (tb) tb[idx] = (float)fmin(kFltMax, fmax(-kFltMax, db));
-  if (tm) tm[idx] = (float)fmin(kFltMax, fmax(-kFltMax, dm));
+  if (ta) ta[idx] = (float)fmin(kFltMax, fmax(-kFltMax, D.da));
+  if (tb) tb[idx] = (float)fmin(kFltMax, fmax(-kFltMax, D.db));
+  if (tm) tm[idx] = (float)fmin(kFltMax, fmax(-kFltMax, D.dm));
 }
 
 }  // namespace
