@@ -110,8 +110,16 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   constexpr int NCOPY = (DH == 64 && NQB == 1) ? 2 : 4;
   constexpr bool RING = NCOPY == 2;               // two copies: the window is the shared ring
   static_assert(!RING || TW == 192, "the ring holds windows of three 64-entry segments");
-  constexpr int WPW = RING ? 1 : NCOPY * (TW / 64) / 4;   // window loads per wave per tile
-  static_assert(RING || NCOPY * (TW / 64) % 4 == 0, "window loads split over four waves");
+  // Four copies: the window lives in an eight-slot ring of 64-entry segments per copy (a
+  // tile's TW / 64 segments, consecutive tiles sharing all but one), slots 0 .. NSEG - 2
+  // mirrored after slot 7 so every window is contiguous.  Each tile adds one segment per
+  // copy: wave w loads copy w's, and its mirror (or the segment again where the slot has
+  // none), so every wave issues two window loads per tile.
+  constexpr int NSEG = TW / 64;
+  constexpr int R4STRIDE = 64 * (8 + NSEG - 1) + 16;   // floats between copies (16 mod 64: 4c bank groups apart)
+  static_assert(RING || NSEG + 2 <= 8, "three tiles in flight must fit the eight slots");
+  static_assert(R4STRIDE % 64 == 16, "ring copies share banks");
+  constexpr int WPW = RING ? 1 : 2;     // window loads per wave per tile
   constexpr int KVL = 2 * CPW;          // K / V direct loads per wave per tile
   constexpr int LPT = KVL + WPW;        // direct-load instructions per wave per tile
   // Two 32-row blocks per wave: each block of MFMAs is issued at raised wave priority, so
@@ -122,12 +130,13 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   static_assert(LPT < 64, "vmcnt range");
 
   // the buffers as distinct objects: the tile being read, and one (ring) or two being filled
-  using Tile = FwdTile<DH, RING ? 0 : NCOPY * (TW + 16)>;
+  using Tile = FwdTile<DH, 0>;
   __shared__ __attribute__((aligned(16))) Tile tA, tB;
   typedef typename std::conditional<RING, uint32_t[4], Tile>::type ThirdTile;   // unused with the ring
   __shared__ __attribute__((aligned(16))) ThirdTile tCst;
   Tile& tC = *reinterpret_cast<Tile*>(&tCst);
-  __shared__ __attribute__((aligned(16))) float wring[RING ? NCOPY * kStripStride : 4];   // ring or strip
+  // the two-copy ring or strip, or the four-copy ring
+  __shared__ __attribute__((aligned(16))) float wring[RING ? NCOPY * kStripStride : NCOPY * R4STRIDE];
 
   const int BH = a.B * a.H;
   // Work-group i runs on XCD i % 8 (one L2 each).  With B * H a multiple of 8 every query
@@ -210,7 +219,18 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     const int row = p / KCH;
     return (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
   };
-  auto issue_tile = [&](Tile& tl, int j0) {
+  // Four-copy ring: segment g (entries from tile 0's window start + 64 g) of copy wave into
+  // slot g & 7, and into its mirror where mirror is set and the slot has one (else the slot
+  // again: the same bytes to the same place).
+  const int u0_first = a.tab_d0 - (i0 + MQ - 1 - jb);   // tile 0's window start in the reversed table
+  auto ring4_load = [&](int g, bool mirror) {
+    const int slot = g & 7;
+    const int pos = (mirror && slot < NSEG - 1) ? 64 * (8 + slot) : 64 * slot;
+    lds_dma4(rW, lane * 4, (u0_first + wave + 64 * g) * 4, &wring[wave * R4STRIDE + pos]);
+  };
+  // the direct loads of local tile t: its K and V, and (four copies) the segment it adds
+  auto issue_tile = [&](Tile& tl, int t) {
+    const int j0 = jb + t * kNK;
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       const int p0 = (wave * CPW + r) * 64;
@@ -219,13 +239,8 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       lds_dma16(rV, vo, 0, &tl.v[p0 * 8]);
     }
     if constexpr (!RING) {
-      const int u0 = a.tab_d0 - (i0 + MQ - 1 - j0);   // window start in the reversed table
-#pragma unroll
-      for (int r = 0; r < WPW; ++r) {
-        const int x = wave * WPW + r;                 // copy x / (TW / 64), segment x % (TW / 64)
-        const int cpy = x / (TW / 64), seg = x % (TW / 64);
-        lds_dma4(rW, lane * 4, (u0 + cpy + 64 * seg) * 4, &tl.w[cpy * (TW + 16) + 64 * seg]);
-      }
+      ring4_load(t + NSEG - 1, false);
+      ring4_load(t + NSEG - 1, true);
     }
   };
   // Ring segment k of local tile t (entries from the window start + 64 k) into slot
@@ -305,7 +320,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
 #pragma unroll
       for (int qb2 = 0; qb2 < NQB; ++qb2) {
         if constexpr (NCOPY == 4) {
-          const f32x4* __restrict__ wv = (const f32x4*)&tl.w[wcopy * (TW + 16)];
+          const f32x4* __restrict__ wv = (const f32x4*)&wring[wcopy * R4STRIDE + 64 * (t & 7)];
           const int y4 = ((ybase - wcopy) >> 2) + 8 * (kb - qb2);   // 16-byte units
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -484,7 +499,14 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       ring_load(0, idx < 3 ? idx : idx - 3, x / 5, idx >= 3);
     }
   }
-  issue_tile(tA, jb);
+  if constexpr (!RING) {   // tile 0's window but its last segment (which issue_tile adds)
+#pragma unroll
+    for (int g = 0; g < NSEG - 1; ++g) {
+      ring4_load(g, false);
+      ring4_load(g, true);
+    }
+  }
+  issue_tile(tA, 0);
   {
     const i32x4 rQ = buffer_rsrc(Q, (uint32_t)T * DH * 2);
 #pragma unroll
@@ -500,7 +522,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   }
   if (RING && a.bias_inkernel) fill_strip();
   if (!RING && ntiles > 1) {
-    issue_tile(tB, jb + kNK);
+    issue_tile(tB, 1);
     BAM_WAIT_VMCNT(LPT);       // tile 0 and Q landed (tile 1 may be in flight)
   } else {
     BAM_WAIT_VMCNT(0);
@@ -524,14 +546,14 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) {
         if (ring) ring_next(t + 1);
-        issue_tile(tB, jb + (t + 1) * kNK);
+        issue_tile(tB, t + 1);
       }
       compute_tile(tA, t);
       advance();
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) {
         if (ring) ring_next(t + 2);
-        issue_tile(tA, jb + (t + 2) * kNK);
+        issue_tile(tA, t + 2);
       }
       compute_tile(tB, t + 1);
       advance();
@@ -539,15 +561,15 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   } else {
     // Three stages: tile t is computed while tiles t + 1 and t + 2 load.
     for (int t = 0; t < ntiles; t += 3) {
-      if (t + 2 < ntiles) issue_tile(tC, jb + (t + 2) * kNK);
+      if (t + 2 < ntiles) issue_tile(tC, t + 2);
       compute_tile(tA, t);
       advance();
       if (t + 1 >= ntiles) break;
-      if (t + 3 < ntiles) issue_tile(tA, jb + (t + 3) * kNK);
+      if (t + 3 < ntiles) issue_tile(tA, t + 3);
       compute_tile(tB, t + 1);
       advance();
       if (t + 2 >= ntiles) break;
-      if (t + 4 < ntiles) issue_tile(tB, jb + (t + 4) * kNK);
+      if (t + 4 < ntiles) issue_tile(tB, t + 4);
       compute_tile(tC, t + 2);
       advance();
     }
