@@ -476,11 +476,24 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   float* ta = (float*)(ws + L.ta_off);
   float* tb = (float*)(ws + L.tb_off);
   float* tm = dmu ? (float*)(ws + L.tm_off) : nullptr;
-  hipError_t e = bam::launch_prior_table_ex(alpha, beta, mu, prior_kind(flags), H, L.g.d0, -1, L.g.n,
-                                            L.g.stride, causal ? 0 : -(T - 1), T - 1, std::sqrt((float)Dh),
-                                            tab, ta, tb, tm, st);
-  if (e != hipSuccess) return BAM_EHIP;
+  // Up to kFwdStripT both kernels compute the alpha and reference priors' bias and
+  // derivatives themselves; no table launch.
+  const int kind = prior_kind(flags);
+  const bool inkernel = T <= bam::kFwdStripT && kind != bam::kPriorSandwich;
+  if (!inkernel) {
+    hipError_t e = bam::launch_prior_table_ex(alpha, beta, mu, kind, H, L.g.d0, -1, L.g.n, L.g.stride,
+                                              causal ? 0 : -(T - 1), T - 1, std::sqrt((float)Dh), tab, ta, tb, tm,
+                                              st);
+    if (e != hipSuccess) return BAM_EHIP;
+  }
   bam::BwdArgs a;
+  a.bias_inkernel = inkernel;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.mu = mu;
+  a.kind = kind;
+  a.dlo = causal ? 0 : -(T - 1);
+  a.dhi = T - 1;
   a.q = q;
   a.k = k;
   a.v = v;

@@ -155,6 +155,14 @@ struct BwdArgs {
   float* dbeta;
   float* dmu;            // null: not computed
   float* ds;
+  // Up to kFwdStripT, for the alpha and reference priors, both kernels compute the bias and
+  // derivative windows themselves (bias_inkernel): the head's parameters, the prior kind and
+  // the visible distance range [dlo, dhi]; the tables are then not read.
+  bool bias_inkernel;
+  const float* alpha;
+  const float* beta;
+  const float* mu;
+  int kind, dlo, dhi;
 };
 
 size_t bwd_param_partials(int B, int H, int T);

@@ -32,6 +32,7 @@
 
 #include "bam_device.h"
 #include "bam_internal.h"
+#include "prior_eval.h"
 
 namespace bam {
 
@@ -41,6 +42,12 @@ constexpr int kQT = 64;      // queries per tile (dkdv)
 constexpr int kKB = 128;     // keys per work-group (dkdv)
 constexpr int kMQ = 128;     // queries per work-group (dq)
 constexpr int kNK = 64;      // keys per tile (dq)
+// The strips (bias_inkernel, T <= kFwdStripT): a work-group computes the window entries of
+// all its tiles once, before its first tile, into LDS: 64 (ntiles + 2) <= kBwdStrip entries
+// per table, consecutive tiles' windows 64 entries apart.  The float32 values are within a
+// few ulps of the float64-derived tables (prior_derivs_f32).
+constexpr int kBwdStrip = 64 * (kFwdStripT / 64 + 2);
+constexpr int kBwdStripStride = kBwdStrip + 16;
 
 // ------------------------------------------------------------------------------------
 // ------------------------------------------------------------------------------------
@@ -88,6 +95,7 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
   // SIMD, fit a CU.  The third wave hides the MFMA -> exp -> MFMA chain that two waves left
   // exposed; 14% faster than three pipeline stages at two waves per SIMD.
   __shared__ __attribute__((aligned(16))) BwdQTile<DH> tA, tB;
+  __shared__ float wstrip[kBwdStrip];   // the bias strip (bias_inkernel)
 
   const int BH = a.B * a.H;
   const int kb = blockIdx.x / BH;
@@ -152,13 +160,30 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
       lds_dma16(rO, voff[r] + i0 * DH * 2, 0, &tl.o[p0 * 8]);
     }
     // the window (three 64-entry segments from the entry of d_max = i0 + kQT - 1 - j0) and
-    // the four row-scalar arrays: seven 256-byte loads, two per wave (the eighth repeats one)
-    const int e0 = a.tab_d0 - (i0 + kQT - 1 - j0);
+    // the four row-scalar arrays: seven 256-byte loads, two per wave (the eighth repeats one);
+    // with the strip only the row scalars, one per wave
+    if (a.bias_inkernel) {
+      lds_dma4(rR, lane * 4, ((uint32_t)wave * nrs + (uint32_t)i0) * 4u, &tl.rs[wave][0]);
+    } else {
+      const int e0 = a.tab_d0 - (i0 + kQT - 1 - j0);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int x = min(2 * wave + r, 6);
-      if (x < 3) lds_dma4(rW, lane * 4, (e0 + 64 * x) * 4, &tl.w[64 * x]);
-      else lds_dma4(rR, lane * 4, ((uint32_t)(x - 3) * nrs + (uint32_t)i0) * 4u, &tl.rs[x - 3][0]);
+      for (int r = 0; r < 2; ++r) {
+        const int x = min(2 * wave + r, 6);
+        if (x < 3) lds_dma4(rW, lane * 4, (e0 + 64 * x) * 4, &tl.w[64 * x]);
+        else lds_dma4(rR, lane * 4, ((uint32_t)(x - 3) * nrs + (uint32_t)i0) * 4u, &tl.rs[x - 3][0]);
+      }
+    }
+  };
+  // The strip: the windows of query tiles qstart, qstart + 64, ... start at decreasing table
+  // entries; strip entry x is table entry e_last + x, e_last that of the last tile, so the
+  // window of tile i0 starts at strip entry (qstart + 64 (ntiles - 1)) - i0.
+  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters, loaded before any tile load
+  const int e_last = a.tab_d0 - (qstart + (ntiles - 1) * kQT + kQT - 1 - j0);
+  auto fill_strip = [&]() {
+    const float sc = __builtin_sqrtf((float)DH);
+    for (int x = tid; x < kBwdStrip; x += 256) {
+      const int d = a.tab_d0 - (e_last + x);
+      wstrip[x] = (d >= a.dlo && d <= a.dhi) ? prior_bias_f32(a.kind, pa, pb, pm, d) * sc : kNegInf;
     }
   };
 
@@ -206,9 +231,10 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
       // qrow and key 32 wave + ql: y = kQT - 1 - qrow + 32 wave + ql.
       f32x16 s, dp;
       const int ybase = kQT - 1 + 32 * wave + ql - 32 * qb - 4 * hh;
+      const float* wsrc = a.bias_inkernel ? &wstrip[qstart + (ntiles - 1) * kQT - i0] : tl.w;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        s[x] = tl.w[ybase - 8 * (x >> 2) - (x & 3)];
+        s[x] = wsrc[ybase - 8 * (x >> 2) - (x & 3)];
         dp[x] = 0.f;
       }
       __builtin_amdgcn_s_setprio(1);
@@ -262,10 +288,16 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
 
   // two-stage pipeline: tile t + 1 loads while tile t is computed; each wave waits for its
   // own loads, then the barrier publishes the tile
+  if (a.bias_inkernel) {
+    pa = a.alpha[h];
+    pb = a.beta[h];
+    pm = a.mu ? a.mu[h] : 0.f;
+  }
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, qstart);
+  if (a.bias_inkernel) fill_strip();   // while tile 0 loads
   BAM_WAIT_VMCNT(0);
-  BAM_BARRIER_VMCNT(63);       // publish tile 0
+  BAM_BARRIER_VMCNT(63);       // publish tile 0 (and the strip)
   for (int t = 0; t < ntiles; t += 2) {
     if (t + 1 < ntiles) issue_tile(tB, qstart + (t + 1) * kQT);
     compute(tA, qstart + t * kQT);
@@ -327,6 +359,7 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
   // three pipeline stages at two waves per SIMD.
   __shared__ __attribute__((aligned(16))) BwdKTile<DH> tA, tB;
   __shared__ float red[4][4];
+  __shared__ float wstr[4][kBwdStripStride];   // bias and derivative strips (bias_inkernel)
 
   const int BH = a.B * a.H;
   const int qb = blockIdx.x / BH;
@@ -447,6 +480,8 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
       lds_dma16(rV, voff[r] + j0 * DH * 2, 0, &tl.v[p0 * 8]);
     }
     // table windows: three 64-entry segments each from the entry of d_max = i0 + kMQ - 1 - j0
+    // (none with the strips)
+    if (a.bias_inkernel) return;
     const int e0 = a.tab_d0 - (i0 + kMQ - 1 - j0);
 #pragma unroll
     for (int r = 0; r < WPW; ++r) {
@@ -492,10 +527,35 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
     return __builtin_bit_cast(bf16x8, vv);
   };
 
+  // The strips: the window of key tile j0 starts at strip entry j0 (entry x is table entry
+  // e_first + x, e_first that of tile 0).
+  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters, loaded before any tile load
+  auto fill_strips = [&]() {
+    const int e_first = a.tab_d0 - (i0 + kMQ - 1);
+    const float sc = __builtin_sqrtf((float)DH);
+    for (int x = (int)threadIdx.x; x < kBwdStrip; x += 256) {
+      const int d = a.tab_d0 - (e_first + x);
+      float bv = kNegInf, da = 0.f, dbe = 0.f, dm = 0.f;
+      if (d >= a.dlo && d <= a.dhi) {
+        prior_derivs_f32(a.kind, pa, pb, pm, d, bv, da, dbe, dm);
+        bv *= sc;
+      }
+      wstr[0][x] = bv;
+      wstr[1][x] = da;
+      wstr[2][x] = dbe;
+      if (MU) wstr[3][x] = dm;
+    }
+  };
+
   auto compute = [&](const BwdKTile<DH>& tl, int j0) __attribute__((always_inline)) {
     // Causal: every key of the tile follows this wave's queries.  Otherwise the second test
     // never holds; the branch keeps the tile a scheduling region of its own.
     if ((CAUSAL && j0 > i0 + 32 * wave + 31) || (!CAUSAL && j0 >= T)) return;
+    const bool ik = a.bias_inkernel;
+    const float* w0 = ik ? &wstr[0][j0] : tl.w[0];
+    const float* w1 = ik ? &wstr[1][j0] : tl.w[1];
+    const float* w2 = ik ? &wstr[2][j0] : tl.w[2];
+    const float* w3 = ik ? &wstr[3][j0] : tl.w[3];
     u32x4 zf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -506,7 +566,7 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
       f32x16 s, dp;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        s[x] = tl.w[0][ybase + 8 * (x >> 2) + (x & 3)];
+        s[x] = w0[ybase + 8 * (x >> 2) + (x & 3)];
         dp[x] = 0.f;
       }
       __builtin_amdgcn_s_setprio(1);
@@ -529,9 +589,9 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
         zv[x] = z;
         const int y = ybase + 8 * (x >> 2) + (x & 3);
         const float cz = c * z;
-        ga = fmaf(cz, tl.w[1][y], ga);
-        gb = fmaf(cz, tl.w[2][y], gb);
-        if (MU) gm = fmaf(cz, tl.w[3][y], gm);
+        ga = fmaf(cz, w1[y], ga);
+        gb = fmaf(cz, w2[y], gb);
+        if (MU) gm = fmaf(cz, w3[y], gm);
         gs = fmaf(z * lnn_sd, fmaxf(sx, -FLT_MAX), gs);
       }
 #pragma unroll
@@ -548,10 +608,16 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
   };
 
   // two-stage pipeline, as the dK / dV kernel
+  if (a.bias_inkernel) {
+    pa = a.alpha[h];
+    pb = a.beta[h];
+    pm = a.mu ? a.mu[h] : 0.f;
+  }
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, 0);
+  if (a.bias_inkernel) fill_strips();   // while tile 0 loads
   BAM_WAIT_VMCNT(0);
-  BAM_BARRIER_VMCNT(63);       // publish tile 0
+  BAM_BARRIER_VMCNT(63);       // publish tile 0 (and the strips)
   for (int t = 0; t < ntiles; t += 2) {
     if (t + 1 < ntiles) issue_tile(tB, (t + 1) * kNK);
     compute(tA, t * kNK);

@@ -10,6 +10,7 @@
 // (|x| + eps)^theta_beta.
 #pragma once
 
+#include <float.h>
 #include <hip/hip_runtime.h>
 
 #include "../../include/bam.h"
@@ -92,6 +93,46 @@ __device__ __forceinline__ float prior_bias_f32(int kind, float a, float be, flo
   if (be == 0.f) return -1.f;                                    // 0^0 = 1
   if (u == 0.f) return be > 0.f ? 0.f : -__builtin_huge_valf();  // beta < 0 at u = 0: precondition violated
   return -__builtin_amdgcn_exp2f(be * __builtin_amdgcn_logf(u));
+}
+
+// b(d) and its three parameter derivatives in float32 (prior_bias_at's cases and formulas),
+// the derivatives saturated at +-FLT_MAX as the distance-table kernel stores them (where
+// u^beta overflows the bias is -inf and the weight exactly 0, and the backward's product
+// 0 * derivative must stay 0).
+__device__ __forceinline__ void prior_derivs_f32(int kind, float a, float be, float m, int d, float& b, float& da,
+                                                 float& db, float& dm) {
+  constexpr float kLn2f = 0.6931471805599453f, kLog2ef = 1.4426950408889634f;
+  da = db = dm = 0.f;
+  if (kind == kPriorRef) {
+    const float em = __expf(m), emi = __expf(-m);
+    const float x = -(float)d - (em - emi);
+    const float g = fabsf(x) + (float)BAM_REF_EPS;
+    const float l2g = __builtin_amdgcn_logf(g);
+    b = -__builtin_amdgcn_exp2f(fmaf(be, l2g, a * kLog2ef));
+    da = b;
+    db = b * l2g * kLn2f;   // b ln g
+    const float sg = x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f);
+    dm = -b * be * sg / g * (em + emi);
+  } else {
+    const float x = (float)d - m;
+    const float u = __builtin_isinf(a) ? 0.f : fabsf(x) / a;
+    if (be == 0.f) {
+      b = -1.f;                                              // 0^0 = 1
+      if (u != 0.f) db = -__builtin_amdgcn_logf(u) * kLn2f;  // -ln u
+    } else if (u == 0.f) {
+      b = be > 0.f ? 0.f : -__builtin_huge_valf();
+    } else {
+      const float l2u = __builtin_amdgcn_logf(u);
+      const float p = __builtin_amdgcn_exp2f(be * l2u);
+      b = -p;
+      da = be * p / a;
+      db = -p * l2u * kLn2f;   // -p ln u
+      dm = be * p / x;         // db/dmu, dx/dmu = -1
+    }
+  }
+  da = fminf(FLT_MAX, fmaxf(-FLT_MAX, da));
+  db = fminf(FLT_MAX, fmaxf(-FLT_MAX, db));
+  dm = fminf(FLT_MAX, fmaxf(-FLT_MAX, dm));
 }
 
 }  // namespace bam
