@@ -628,8 +628,8 @@ def main():
                              "frac": round(r["bwd_gbs"] / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes_per_call": r["bwd_bytes"],
                              "pct_mfma_peak": round(100 * r["bwd_tflops"] / PEAK_BF16_TFLOPS, 2),
-                             "note": "whole backward call (table + bwd_dq + bwd_dkdv): Q, K, V, O, dO read, "
-                                     "dQ, dK, dV written (bf16) and lse read"}}
+                             "note": "whole backward call (bwd_dq + bwd_dkdv; no table launch at T <= 512): "
+                                     "Q, K, V, O, dO read, dQ, dK, dV written (bf16) and lse read"}}
         if "train512" in parts:
             r = bench_train_step(torch, w3, args.steps, args.warmup, timer)
             out_parts["train_step_T512"] = {
