@@ -166,8 +166,9 @@ def bench_skip(torch, bam, w, steps, timer):
     without it, table prebuilt in both (the skipping plan's kernels are inside the timed
     call).  Two prior settings: the workload's own heads, and the pages' AttentionPrior
     initialisation in the reference form (theta_alpha = ALiBi slopes, theta_beta =
-    linspace(0, 1), theta_mu = 0, s = 1 / ln 512).  Skipping changes the work, not the
-    result, so these figures are kept apart from the algorithmic-flop metric."""
+    linspace(0, 1), theta_mu = 0, s = 1 / ln 512).  The backward call with and without
+    skipping as well.  Skipping changes the work, not the result, so these figures are kept
+    apart from the algorithmic-flop metric."""
     x = device_inputs(torch, w)
     B, H, T, Dh = w.q.shape
     o = torch.empty((B, H, T, Dh), dtype=torch.bfloat16, device="cuda")
@@ -194,6 +195,21 @@ def bench_skip(torch, bam, w, steps, timer):
         out[name] = {"skipped_tile_fraction": round(frac, 4), "full_ms": round(full, 4), "skip_ms": round(skip, 4),
                      "speedup": round(full / skip, 3),
                      "effective_TFLOP/s": round(flops / skip / 1e9, 1)}
+        # the backward call with and without skipping (its own plan over 128-query blocks
+        # inside the timed call), gradients for every input and parameter
+        call(False)
+        dout = torch.randn((B, H, T, Dh), generator=torch.Generator(device="cuda").manual_seed(2), device="cuda",
+                           dtype=torch.float32).to(torch.bfloat16)
+        wsb = torch.empty(bam.bam_bwd_workspace_size(B, H, T, Dh, flags), dtype=torch.uint8, device="cuda")
+
+        def bwd(skip_far):
+            bam.bam_attn_bwd_ex(x["q"], x["k"], x["v"], o, lse, dout, p["alpha"], p["beta"], p["mu"], p["s"],
+                                causal=True, ssmax=True, workspace=wsb, prior_ref=ref, skip_far=skip_far)
+        bfull = timer.per_launch(lambda: bwd(False), max(2, steps // 2))
+        bskip = timer.per_launch(lambda: bwd(True), max(2, steps // 2))
+        log(f"[skip32k:{name}] backward full {bfull:.4f} ms, skipping {bskip:.4f} ms")
+        out[name].update({"bwd_full_ms": round(bfull, 4), "bwd_skip_ms": round(bskip, 4),
+                          "bwd_speedup": round(bfull / bskip, 3)})
     return out
 
 

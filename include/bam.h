@@ -103,7 +103,8 @@ typedef int bam_status;
  * backward's dalpha, dbeta and dmu are zero.  Not combinable with BAM_PRIOR_REF
  * (BAM_EINVAL).  Accepted by every entry point. */
 #define BAM_PRIOR_SANDWICH 16u
-/* Prior-aware key skipping (bam_attn_fwd, causal bf16 only; BAM_EUNSUPPORTED otherwise).
+/* Prior-aware key skipping (bam_attn_fwd and the backward, causal bf16 only;
+ * BAM_EUNSUPPORTED otherwise).
  * For each block of query rows the call first bounds every logit from above,
  *   l_ij <= c_i (|q_i| max_j |k_j| / sqrt(Dh) + max_{d >= i - j} b(d)),
  * and the row maximum from below by the diagonal logit l_ii, then leaves out the leading
@@ -113,7 +114,11 @@ typedef int bam_status;
  * precision, while a prior that decays with distance (beta > 0 local heads) saves the far
  * tiles.  Rows with c_i <= 0 and non-finite bounds never skip; the bound assumes finite
  * q, k and bias.  Needs the larger workspace that bam_fwd_workspace_size reports for
- * these flags. */
+ * these flags.  The backward plans the same way over 128-query blocks: the dQ pass starts
+ * each block's key loop at its first needed tile, and the dK / dV pass leaves out the query
+ * tiles of blocks whose first needed tile lies beyond its keys.  Every term it leaves out is
+ * zero in float32 (its weight is, so its dZ is), so dQ, dK, dV and the parameter gradients
+ * equal those of the full backward bit for bit (bam_bwd_workspace_size with the flag). */
 #define BAM_SKIP_FAR 32u
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -548,25 +548,26 @@ def bam_attn_decode_paged(q, k_pages, v_pages, block_table, kv_len, alpha, beta,
 
 def bam_attn_bwd(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
                  grad_dtype=None, workspace=None, stream=None, prior_ref=False,
-                 prior=None):
-    """Backward.  Returns (dq, dk, dv, dalpha, dbeta, ds)."""
+                 prior=None, skip_far=False):
+    """Backward.  Returns (dq, dk, dv, dalpha, dbeta, ds).  skip_far: leave out the key /
+    query tiles whose weights are zero in float32 (BAM_SKIP_FAR; causal only)."""
     return _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream,
-                prior_ref, False, prior)
+                prior_ref, False, prior, skip_far)
 
 
 def bam_attn_bwd_ex(q, k, v, o, lse, dout, alpha, beta, mu=None, s=None, causal=True, ssmax=True,
                     grad_dtype=None, workspace=None, stream=None, prior_ref=False,
-                 prior=None):
+                    prior=None, skip_far=False):
     """Backward with the offset gradient.  Returns (dq, dk, dv, dalpha, dbeta, dmu, ds)."""
     return _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream,
-                prior_ref, True, prior)
+                prior_ref, True, prior, skip_far)
 
 
 def _bwd(q, k, v, o, lse, dout, alpha, beta, mu, s, causal, ssmax, grad_dtype, workspace, stream, prior_ref,
-         want_mu, prior=None):
+         want_mu, prior=None, skip_far=False):
     torch = _torch()
     B, H, T, Dh = _shape(q, "q", 4)
-    flags = _flags(causal, ssmax, prior_ref, prior)
+    flags = _flags(causal, ssmax, prior_ref, prior) | (BAM_SKIP_FAR if skip_far else 0)
     in_code = _dtype_code(q)
     dev = q.device
     for name, t in (("k", k), ("v", v), ("dout", dout)):

@@ -409,15 +409,20 @@ bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void*
 // ---------------------------------------------------------------------------------------
 namespace {
 // Backward workspace: the four distance tables (forward layout), the per-row scalars of the
-// dK / dV kernel (four arrays over rows padded to 64) and the parameter partials.
+// dK / dV kernel (four arrays over rows padded to 64) and the parameter partials; with
+// BAM_SKIP_FAR (causal) then the skipping plan's arrays, planned per 128-query block.
 struct BwdLayout {
   size_t tab_off, ta_off, tb_off, tm_off, rs_off, part_off, total;
-  int Tp;
+  size_t smax_off, rowu_off, rowv_off, kpart_off, first_off;
+  int Tp, nqb, nparts;
   TableGeom g;
 };
 
-BwdLayout bwd_layout(int B, int H, int T, bool causal) {
-  BwdLayout L;
+constexpr int kBwdPlanRows = 128;   // query rows per block of the backward's skipping plan
+
+BwdLayout bwd_layout(int B, int H, int T, int Dh, unsigned flags) {
+  const bool causal = (flags & BAM_CAUSAL) != 0;
+  BwdLayout L{};
   L.g = fwd_table_geom(T, causal);
   const size_t tabsz = align_up((size_t)H * L.g.stride * sizeof(float));
   L.Tp = (T + 63) / 64 * 64;
@@ -428,14 +433,24 @@ BwdLayout bwd_layout(int B, int H, int T, bool causal) {
   L.rs_off = 4 * tabsz;
   L.part_off = L.rs_off + align_up((size_t)4 * B * H * L.Tp * sizeof(float));
   L.total = L.part_off + align_up(bam::bwd_param_partials(B, H, T) * sizeof(float));
+  if ((flags & BAM_SKIP_FAR) && causal && Dh > 0 && Dh % 8 == 0 && Dh <= 128) {
+    const size_t BH = (size_t)B * H;
+    L.nqb = (T + kBwdPlanRows - 1) / kBwdPlanRows;
+    L.nparts = (T + bam::skip_rows_per_block(Dh) - 1) / bam::skip_rows_per_block(Dh);
+    L.smax_off = L.total;
+    L.rowu_off = L.smax_off + align_up((size_t)H * T * sizeof(float));
+    L.rowv_off = L.rowu_off + align_up(BH * T * sizeof(float));
+    L.kpart_off = L.rowv_off + align_up(BH * T * sizeof(float));
+    L.first_off = L.kpart_off + align_up(BH * L.nparts * sizeof(float));
+    L.total = L.first_off + align_up(BH * L.nqb * sizeof(int32_t));
+  }
   return L;
 }
 }  // namespace
 
 size_t bam_bwd_workspace_size(int B, int H, int T, int Dh, unsigned flags) {
-  (void)Dh;
   if (!dims_ok(B, H, T)) return 0;
-  return bwd_layout(B, H, T, (flags & BAM_CAUSAL) != 0).total;
+  return bwd_layout(B, H, T, Dh, flags).total;
 }
 
 bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
@@ -459,8 +474,9 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
       dalpha == nullptr || dbeta == nullptr || ds == nullptr || workspace == nullptr ||
       !prior_ok(alpha, beta, s, flags))
     return BAM_EINVAL;
-  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | kPriorFlags)) != 0) return BAM_EINVAL;
+  if ((flags & ~(BAM_CAUSAL | BAM_SSMAX | kPriorFlags | BAM_SKIP_FAR)) != 0) return BAM_EINVAL;
   if (in_dtype != BAM_BF16 || (Dh != 32 && Dh != 64)) return BAM_EUNSUPPORTED;
+  if ((flags & BAM_SKIP_FAR) && !(flags & BAM_CAUSAL)) return BAM_EUNSUPPORTED;
   if ((o_dtype != BAM_BF16 && o_dtype != BAM_F32) || (grad_dtype != BAM_BF16 && grad_dtype != BAM_F32))
     return BAM_EUNSUPPORTED;
   // the dK / dV kernel's buffer loads address one (b, h) of Q / dO and all four row-scalar
@@ -468,7 +484,8 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   if ((size_t)T * Dh * 2 > 0x7fffffffu || (size_t)16 * B * H * ((T + 63) / 64 * 64) > 0x7fffffffu)
     return BAM_EUNSUPPORTED;
   const bool causal = (flags & BAM_CAUSAL) != 0;
-  const BwdLayout L = bwd_layout(B, H, T, causal);
+  const bool skip = (flags & BAM_SKIP_FAR) != 0;
+  const BwdLayout L = bwd_layout(B, H, T, Dh, flags);
   if (workspace_bytes < L.total) return BAM_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -477,10 +494,10 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   float* tb = (float*)(ws + L.tb_off);
   float* tm = dmu ? (float*)(ws + L.tm_off) : nullptr;
   // Up to kFwdStripT both kernels compute the alpha and reference priors' bias and
-  // derivatives themselves; no table launch.
+  // derivatives themselves; no table launch unless the skipping plan needs the table.
   const int kind = prior_kind(flags);
   const bool inkernel = T <= bam::kFwdStripT && kind != bam::kPriorSandwich;
-  if (!inkernel) {
+  if (!inkernel || skip) {
     hipError_t e = bam::launch_prior_table_ex(alpha, beta, mu, kind, H, L.g.d0, -1, L.g.n, L.g.stride,
                                               causal ? 0 : -(T - 1), T - 1, std::sqrt((float)Dh), tab, ta, tb, tm,
                                               st);
@@ -525,6 +542,28 @@ bam_status bam_attn_bwd_ex(const void* q, const void* k, const void* v, const vo
   a.dbeta = dbeta;
   a.dmu = dmu;
   a.ds = ds;
+  a.first_tile = nullptr;
+  if (skip) {
+    // the forward's plan over 128-query blocks (the dQ kernel's): the first key tile each
+    // block needs; the dK / dV kernel leaves out the query tiles of blocks that start
+    // beyond its keys
+    bam::SkipArgs sk;
+    sk.q = q;
+    sk.k = k;
+    sk.tab = tab;
+    sk.tab_d0 = L.g.d0;
+    sk.tab_stride = L.g.stride;
+    sk.s = s;
+    sk.ssmax = a.ssmax;
+    sk.smax = (float*)(ws + L.smax_off);
+    sk.rowu = (float*)(ws + L.rowu_off);
+    sk.rowv = (float*)(ws + L.rowv_off);
+    sk.kpart = (float*)(ws + L.kpart_off);
+    sk.first_tile = (int32_t*)(ws + L.first_off);
+    hipError_t e = bam::launch_fwd_skip_plan(sk, B, H, T, Dh, kBwdPlanRows, st);
+    if (e != hipSuccess) return BAM_EHIP;
+    a.first_tile = sk.first_tile;
+  }
   return hip_status(bam::launch_bwd(a, Dh, st));
 }
 

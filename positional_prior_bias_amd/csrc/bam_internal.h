@@ -163,6 +163,9 @@ struct BwdArgs {
   const float* beta;
   const float* mu;
   int kind, dlo, dhi;
+  // Prior-aware skipping (causal): per 128-query block of each (b, h), the first 64-key
+  // tile that can carry a weight float32 holds (index qb * B * H + b * H + h), or null.
+  const int32_t* first_tile;
 };
 
 size_t bwd_param_partials(int B, int H, int T);

@@ -137,7 +137,23 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
     for (int x = 0; x < 16; ++x) { dk[db][x] = 0.f; dv[db][x] = 0.f; }
 
   const int qstart = CAUSAL ? j0 : 0;
-  const int ntiles = (T - qstart + kQT - 1) / kQT;
+  int ntiles = (T - qstart + kQT - 1) / kQT;
+  // Prior-aware skipping: a query tile whose 128-query block starts (per the plan) at a key
+  // tile beyond this work-group's keys has weight zero in float32 for all of them; its terms
+  // are exactly zero.  The loop ends after the last query block that needs these keys, and
+  // the tiles before it that do not are not computed.
+  const int kt_last = (j0 + kKB - 1) / 64;   // this work-group's last key tile
+  const int32_t* ftp = CAUSAL ? a.first_tile : nullptr;
+  if (ftp) {
+    const int nqb = (T + 127) / 128;
+    int last = -1;
+    for (int qb = j0 / 128 + lane; qb < nqb; qb += 64)
+      if (min(ftp[qb * BH + bh], 2 * qb) <= kt_last) last = qb;   // a block's own keys always count
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    last = __builtin_amdgcn_readfirstlane(last);
+    ntiles = max(0, min(ntiles, (min(T, 128 * (last + 1)) - qstart + kQT - 1) / kQT));
+  }
 
   // direct loads: chunk position p of a tile holds global chunk (row, (p % KCH) ^ swizzle(row))
   const i32x4 rQ = buffer_rsrc(Q, (uint32_t)T * DH * 2);
@@ -224,6 +240,7 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
     // of its own, as in the causal case (one region with the loop around it needs more
     // registers than two waves per SIMD have).
     if ((CAUSAL && i0 + kQT - 1 < jw) || (!CAUSAL && i0 >= T)) return;
+    if (ftp && min(__builtin_amdgcn_readfirstlane(ftp[(i0 / 128) * BH + bh]), 2 * (i0 / 128)) > kt_last) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       __builtin_amdgcn_sched_barrier(0);
@@ -454,7 +471,13 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
   float ga = 0.f, gb = 0.f, gs = 0.f, gm = 0.f;
 
   const int kend = CAUSAL ? min(T, i0 + kMQ) : T;
-  const int ntiles = (kend + kNK - 1) / kNK;
+  // prior-aware skipping: the key tiles before the plan's first tile carry weights that are
+  // zero in float32, so their dZ, and every term they add, is exactly zero
+  int tf = 0;
+  if (CAUSAL && a.first_tile)
+    tf = min(max(__builtin_amdgcn_readfirstlane(a.first_tile[qb * BH + bh]), 0), i0 / kNK);
+  const int jb = tf * kNK;                          // first key of the loop
+  const int ntiles = (kend - jb + kNK - 1) / kNK;
 
   // direct loads: chunk position p of a tile holds global chunk (row, (p % KCH) ^ swizzle(row))
   const i32x4 rK = buffer_rsrc(K, (uint32_t)T * DH * 2);
@@ -614,18 +637,18 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
     pm = a.mu ? a.mu[h] : 0.f;
   }
   BAM_WAIT_VMCNT(0);
-  issue_tile(tA, 0);
+  issue_tile(tA, jb);
   if (a.bias_inkernel) fill_strips();   // while tile 0 loads
   BAM_WAIT_VMCNT(0);
   BAM_BARRIER_VMCNT(63);       // publish tile 0 (and the strips)
   for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) issue_tile(tB, (t + 1) * kNK);
-    compute(tA, t * kNK);
+    if (t + 1 < ntiles) issue_tile(tB, jb + (t + 1) * kNK);
+    compute(tA, jb + t * kNK);
     BAM_WAIT_VMCNT(0);
     BAM_BARRIER_VMCNT(63);
     if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) issue_tile(tA, (t + 2) * kNK);
-    compute(tB, (t + 1) * kNK);
+    if (t + 2 < ntiles) issue_tile(tA, jb + (t + 2) * kNK);
+    compute(tB, jb + (t + 1) * kNK);
     BAM_WAIT_VMCNT(0);
     BAM_BARRIER_VMCNT(63);
   }
