@@ -124,6 +124,13 @@ __device__ __forceinline__ int vswz(int r) {
   return swz_chunk(r, DH / 8 - 1);
 }
 
+// A wave-uniform float read through the constant address space, which the compiler lowers
+// to a scalar load (s_load_dword into an SGPR, waited for on lgkmcnt): it does not queue
+// behind the vector loads in flight, and waiting for it does not wait for them.
+__device__ __forceinline__ float uniform_load(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (expcnt / lgkmcnt left at max)
 #define BAM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 

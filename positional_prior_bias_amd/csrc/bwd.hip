@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
   // The strip: the windows of query tiles qstart, qstart + 64, ... start at decreasing table
   // entries; strip entry x is table entry e_last + x, e_last that of the last tile, so the
   // window of tile i0 starts at strip entry (qstart + 64 (ntiles - 1)) - i0.
-  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters, loaded before any tile load
+  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters (scalar loads in the prologue)
   const int e_last = a.tab_d0 - (qstart + (ntiles - 1) * kQT + kQT - 1 - j0);
   auto fill_strip = [&]() {
     const float sc = __builtin_sqrtf((float)DH);
@@ -305,14 +305,14 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
 
   // two-stage pipeline: tile t + 1 loads while tile t is computed; each wave waits for its
   // own loads, then the barrier publishes the tile
-  if (a.bias_inkernel) {
-    pa = a.alpha[h];
-    pb = a.beta[h];
-    pm = a.mu ? a.mu[h] : 0.f;
-  }
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, qstart);
-  if (a.bias_inkernel) fill_strip();   // while tile 0 loads
+  if (a.bias_inkernel) {   // while tile 0 loads; the head's parameters by scalar loads, whose
+    pa = uniform_load(a.alpha + h);   // wait (lgkmcnt) leaves tile 0 in flight
+    pb = uniform_load(a.beta + h);
+    pm = a.mu ? uniform_load(a.mu + h) : 0.f;
+    fill_strip();
+  }
   BAM_WAIT_VMCNT(0);
   BAM_BARRIER_VMCNT(63);       // publish tile 0 (and the strip)
   for (int t = 0; t < ntiles; t += 2) {
@@ -552,7 +552,7 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
 
   // The strips: the window of key tile j0 starts at strip entry j0 (entry x is table entry
   // e_first + x, e_first that of tile 0).
-  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters, loaded before any tile load
+  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters (scalar loads in the prologue)
   auto fill_strips = [&]() {
     const int e_first = a.tab_d0 - (i0 + kMQ - 1);
     const float sc = __builtin_sqrtf((float)DH);
@@ -631,14 +631,14 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
   };
 
   // two-stage pipeline, as the dK / dV kernel
-  if (a.bias_inkernel) {
-    pa = a.alpha[h];
-    pb = a.beta[h];
-    pm = a.mu ? a.mu[h] : 0.f;
-  }
   BAM_WAIT_VMCNT(0);
   issue_tile(tA, jb);
-  if (a.bias_inkernel) fill_strips();   // while tile 0 loads
+  if (a.bias_inkernel) {   // while tile 0 loads; the head's parameters by scalar loads, whose
+    pa = uniform_load(a.alpha + h);   // wait (lgkmcnt) leaves tile 0 in flight
+    pb = uniform_load(a.beta + h);
+    pm = a.mu ? uniform_load(a.mu + h) : 0.f;
+    fill_strips();
+  }
   BAM_WAIT_VMCNT(0);
   BAM_BARRIER_VMCNT(63);       // publish tile 0 (and the strips)
   for (int t = 0; t < ntiles; t += 2) {

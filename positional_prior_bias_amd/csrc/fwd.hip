@@ -206,19 +206,25 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   const i32x4 rK = buffer_rsrc(K, (uint32_t)T * DH * 2);
   const i32x4 rV = buffer_rsrc(V, (uint32_t)T * DH * 2);
   const i32x4 rW = buffer_rsrc(tabh, (uint32_t)a.tab_stride * 4);
-  // Per-lane byte offset of direct load r.  In the 128-row kernel the offsets are recomputed
-  // at each issue from a lane id the compiler cannot see through: kept live across the tile
-  // they pushed it past its 128 VGPRs, and the spill reloads waited for every load in flight.
+  // Lane id; in the 128-row kernel read by inline assembly, which the compiler cannot hoist,
+  // so the values derived from it (the ring window's offsets, the epilogue's indices) are
+  // recomputed where they are used instead of held in registers across the loop.
   auto issue_lane = [&]() {
     int ln = lane;
     if constexpr (NQB == 1) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     return ln;
   };
   auto kv_voff = [&](int r) {
-    const int p = (wave * CPW + r) * 64 + issue_lane();
-    const int row = p / KCH;
-    return (row * DH + ((p % KCH) ^ vswz<DH>(row)) * 8) * 2;
+    const unsigned p = (unsigned)((wave * CPW + r) * 64) + (unsigned)issue_lane();
+    const unsigned row = p / KCH;
+    return (int)((row * DH + ((p % KCH) ^ (unsigned)vswz<DH>((int)row)) * 8) * 2);
   };
+  // Per-lane byte offsets of the K / V direct loads, computed once (unsigned: no rounding
+  // fix-up for a negative quotient).  Two registers; recomputing them at each issue cost
+  // about 17 VALU instructions per load pair.
+  int kvo[CPW];
+#pragma unroll
+  for (int r = 0; r < CPW; ++r) kvo[r] = kv_voff(r);
   // Four-copy ring: segment g (entries from tile 0's window start + 64 g) of copy wave into
   // slot g & 7, and into its mirror where mirror is set and the slot has one (else the slot
   // again: the same bytes to the same place).
@@ -234,7 +240,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       const int p0 = (wave * CPW + r) * 64;
-      const int vo = kv_voff(r) + j0 * DH * 2;
+      const int vo = kvo[r] + j0 * DH * 2;
       lds_dma16(rK, vo, 0, &tl.k[p0 * 8]);
       lds_dma16(rV, vo, 0, &tl.v[p0 * 8]);
     }
@@ -258,7 +264,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   // float32 (prior_bias_f32: within a few ulps of the table's float64-derived value).
   // Thread l computes table entries u0 + l, u0 + l + 256, ... once and stores each in both
   // copies.  That takes the distance-table launch out of the forward call.
-  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters, loaded before the prologue's loads
+  float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters (scalar loads in the prologue)
   auto fill_strip = [&]() {
     const int u0 = a.tab_d0 - (i0 + MQ - 1 - jb);
     const float sc = __builtin_sqrtf((float)DH);
@@ -484,12 +490,6 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
   // 0 and 1: ten loads, three per wave, the surplus repeating) goes first; each later tile's
   // segment is issued one tile ahead, after the barrier that frees its slot.  The strip is
   // computed while tile 0 and Q load.
-  if (RING && a.bias_inkernel) {
-    // loaded (and waited for) before any tile load is in flight
-    pa = a.alpha[h];
-    pb = a.beta[h];
-    pm = a.mu ? a.mu[h] : 0.f;
-  }
   BAM_WAIT_VMCNT(0);
   if (RING && !a.bias_inkernel) {
 #pragma unroll
@@ -520,7 +520,14 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       }
     }
   }
-  if (RING && a.bias_inkernel) fill_strip();
+  if (RING && a.bias_inkernel) {
+    // scalar loads, issued after tile 0's and Q's: the wait for them (lgkmcnt) leaves those
+    // in flight
+    pa = uniform_load(a.alpha + h);
+    pb = uniform_load(a.beta + h);
+    pm = a.mu ? uniform_load(a.mu + h) : 0.f;
+    fill_strip();
+  }
   if (!RING && ntiles > 1) {
     issue_tile(tB, 1);
     BAM_WAIT_VMCNT(LPT);       // tile 0 and Q landed (tile 1 may be in flight)
