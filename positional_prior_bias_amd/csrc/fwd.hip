@@ -566,18 +566,22 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       advance();
     }
   } else {
-    // Three stages: tile t is computed while tiles t + 1 and t + 2 load.
-    for (int t = 0; t < ntiles; t += 3) {
-      if (t + 2 < ntiles) issue_tile(tC, t + 2);
-      compute_tile(tA, t);
+    // Three stages: tile t is computed while tiles t + 1 and t + 2 load, from buffer t % 3.
+    // Two tiles per iteration, the buffers picked at run time: the compiler keeps O in two
+    // register sets that alternate from tile to tile, so a three-tile body (one per buffer)
+    // ended with O in the other set and 32 64-bit moves to bring it back; a two-tile body
+    // ends where it began.
+    auto buf = [&](int t) -> Tile& {
+      const int r = t % 3;
+      return r == 0 ? tA : (r == 1 ? tB : tC);
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 2 < ntiles) issue_tile(buf(t + 2), t + 2);
+      compute_tile(buf(t), t);
       advance();
       if (t + 1 >= ntiles) break;
-      if (t + 3 < ntiles) issue_tile(tA, t + 3);
-      compute_tile(tB, t + 1);
-      advance();
-      if (t + 2 >= ntiles) break;
-      if (t + 4 < ntiles) issue_tile(tB, t + 4);
-      compute_tile(tC, t + 2);
+      if (t + 3 < ntiles) issue_tile(buf(t + 3), t + 3);
+      compute_tile(buf(t + 1), t + 1);
       advance();
     }
   }
