@@ -142,7 +142,8 @@ struct BwdArgs {
   bool causal, ssmax;
   // Per-row scalars of the dK / dV kernel (written by the dQ kernel), four arrays
   // [B*H][Tp] (Tp = T rounded up to 64): Cl = c log2(e) / sqrt(Dh), L2 = lse log2(e),
-  // D = rowsum(dO * O), Cq = c / sqrt(Dh); rows at or beyond T hold FLT_MIN, +inf, 0, 0.
+  // D Cq with D = rowsum(dO * O), Cq = c / sqrt(Dh); rows at or beyond T hold FLT_MIN,
+  // +inf, 0, 0.
   float* rowsc;
   int Tp;
   float* dq_acc;         // [B,H,T,Dh] fp32 accumulator

@@ -192,14 +192,17 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
   };
   // The strip: the windows of query tiles qstart, qstart + 64, ... start at decreasing table
   // entries; strip entry x is table entry e_last + x, e_last that of the last tile, so the
-  // window of tile i0 starts at strip entry (qstart + 64 (ntiles - 1)) - i0.
+  // window of tile i0 starts at strip entry (qstart + 64 (ntiles - 1)) - i0.  Entry x is
+  // stored at wstrip[kBwdStrip - 1 - x]: a lane's accumulator values (rows 4 g + 0..3) then
+  // come from ascending addresses and are read straight into the accumulator registers (in
+  // the table's order each pair was read reversed and moved into place).
   float pa = 0.f, pb = 0.f, pm = 0.f;   // the head's parameters (scalar loads in the prologue)
   const int e_last = a.tab_d0 - (qstart + (ntiles - 1) * kQT + kQT - 1 - j0);
   auto fill_strip = [&]() {
     const float sc = __builtin_sqrtf((float)DH);
     for (int x = tid; x < kBwdStrip; x += 256) {
       const int d = a.tab_d0 - (e_last + x);
-      wstrip[x] = (d >= a.dlo && d <= a.dhi) ? prior_bias_f32(a.kind, pa, pb, pm, d) * sc : kNegInf;
+      wstrip[kBwdStrip - 1 - x] = (d >= a.dlo && d <= a.dhi) ? prior_bias_f32(a.kind, pa, pb, pm, d) * sc : kNegInf;
     }
   };
 
@@ -248,12 +251,16 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
       // qrow and key 32 wave + ql: y = kQT - 1 - qrow + 32 wave + ql.
       f32x16 s, dp;
       const int ybase = kQT - 1 + 32 * wave + ql - 32 * qb - 4 * hh;
-      const float* wsrc = a.bias_inkernel ? &wstrip[qstart + (ntiles - 1) * kQT - i0] : tl.w;
+      if (a.bias_inkernel) {
+        const float* wr = &wstrip[kBwdStrip - 1 - (qstart + (ntiles - 1) * kQT - i0) - ybase];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        s[x] = wsrc[ybase - 8 * (x >> 2) - (x & 3)];
-        dp[x] = 0.f;
+        for (int x = 0; x < 16; ++x) s[x] = wr[8 * (x >> 2) + (x & 3)];
+      } else {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) s[x] = tl.w[ybase - 8 * (x >> 2) - (x & 3)];
       }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) dp[x] = 0.f;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -273,7 +280,7 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
         const int q4 = 32 * qb + 8 * g + 4 * hh;
         const f32x4 cl4 = *(const f32x4*)&tl.rs[0][q4];
         const f32x4 l24 = *(const f32x4*)&tl.rs[1][q4];
-        const f32x4 d4 = *(const f32x4*)&tl.rs[2][q4];
+        const f32x4 dc4 = *(const f32x4*)&tl.rs[2][q4];
         const f32x4 cq4 = *(const f32x4*)&tl.rs[3][q4];
         float pv[4], zv[4];
 #pragma unroll
@@ -281,7 +288,7 @@ __global__ void __launch_bounds__(256, 3) bwd_dkdv_kernel(BwdArgs a, int nkb, in
           const int x = 4 * g + r;
           const float p = exp2_fast(cl4[r] * s[x] - l24[r]);
           pv[r] = p;
-          zv[r] = p * (dp[x] - d4[r]) * cq4[r];
+          zv[r] = p * fmaf(dp[x], cq4[r], -dc4[r]);   // p (dP - D) c / sqrt(Dh)
         }
         // register x = 8 s' + t, t = 4 (g & 1) + r  ->  operand s', dwords (t >> 1)
         pf[g >> 1][2 * (g & 1) + 0] = pack_bf16x2(pv[0], pv[1]);
@@ -458,7 +465,7 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
     float* rs = a.rowsc + (size_t)bh * a.Tp + i;
     rs[0] = valid ? Cl : FLT_MIN;
     rs[n] = L2;
-    rs[2 * n] = valid ? Di : 0.f;
+    rs[2 * n] = valid ? Di * (c * inv_sqrtD) : 0.f;
     rs[3 * n] = valid ? c * inv_sqrtD : 0.f;
   }
   const float lnn_sd = a.ssmax ? __logf((float)n_i) * inv_sqrtD : 0.f;
@@ -611,11 +618,12 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
         const float z = p * (dp[x] - Di);
         zv[x] = z;
         const int y = ybase + 8 * (x >> 2) + (x & 3);
-        const float cz = c * z;
-        ga = fmaf(cz, w1[y], ga);
-        gb = fmaf(cz, w2[y], gb);
-        if (MU) gm = fmaf(cz, w3[y], gm);
-        gs = fmaf(z * lnn_sd, fmaxf(sx, -FLT_MAX), gs);
+        // the lane's row factors (c for the prior's parameters, ln(n) / sqrt(Dh) for s) are
+        // applied once, after the key loop
+        ga = fmaf(z, w1[y], ga);
+        gb = fmaf(z, w2[y], gb);
+        if (MU) gm = fmaf(z, w3[y], gm);
+        gs = fmaf(z, fmaxf(sx, -FLT_MAX), gs);
       }
 #pragma unroll
       for (int x = 0; x < 16; x += 2) zf[2 * kb + (x >> 3)][(x & 7) >> 1] = pack_bf16x2(zv[x], zv[x + 1]);
@@ -673,6 +681,10 @@ __global__ void __launch_bounds__(256, DH == 64 ? 3 : 2) bwd_dq_kernel(BwdArgs a
       }
   }
   // per-work-group parameter partials (fixed order, no atomics)
+  ga *= c;
+  gb *= c;
+  gm *= c;
+  gs *= lnn_sd;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     ga += __shfl_xor(ga, off, 64);
