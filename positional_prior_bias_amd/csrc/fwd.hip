@@ -22,7 +22,9 @@
 //     with sqrt(Dh) * b(i - j) from a window of the per-head distance table staged in LDS
 //     (stored in reverse distance order, so a lane's values are read in register order),
 //     and the MFMA returns q.k + sqrt(Dh) b directly.  Distances the causal mask forbids
-//     hold -inf in that window, so masking is free as well.
+//     hold -inf in that window, so masking is free as well.  Up to T = 512 (the training
+//     context) a 128-row work-group computes the window entries of all its tiles itself,
+//     into an LDS strip, while its first tile loads, and the call launches no table kernel.
 //   * The running max of a row is exact, so every weight is at most 1 when it is rounded to
 //     bf16 for the PV product (O and l are multiplied by the rescale factor every tile, by
 //     1 when the max holds; this keeps the tile one basic block).
