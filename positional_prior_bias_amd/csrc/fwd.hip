@@ -399,7 +399,7 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
       const float mx = max_xor32(__builtin_fmaxf(mxa, mxb));
       // The running max is exact (not lazy): the largest weight computed so far is then
       // exactly 1 and every weight is at most 1, so rounding P to bf16 perturbs each weight
-      // by at most 2^-9 of itself.  (A lazy max that moved only on jumps of 2^8 let the
+      // by at most 2^-8 of itself.  (A lazy max that moved only on jumps of 2^8 let the
       // dominant weight reach 2^8 and round; O's error then reached 2^-9 max|V|.)  O and
       // l are multiplied by the factor every tile, 1 when the max holds: a branch around
       // the multiply made the compiler copy all of O on every tile to merge the two paths.
