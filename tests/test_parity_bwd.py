@@ -52,6 +52,8 @@ def check(w, got):
     (130, 32, False, False, (0.3, 1.5), 0.0),
     (257, 64, True, True, (0.1, 0.9), 0.0),
     (300, 64, False, True, (-0.8, -0.1), -0.5),
+    (600, 64, True, True, (0.2, 1.2), 0.0),       # T > 512: the windows come from the table
+    (700, 32, False, True, (-0.8, -0.1), -0.5),
 ])
 def test_bwd_random(T, Dh, causal, ssmax, br, mu):
     w = wl.random_case(300 + T, 2, 3, T, Dh, "bf16", wl.CAUSAL * causal | wl.SSMAX * ssmax, beta_range=br, mu=mu,
