@@ -319,9 +319,14 @@ def bench_train_step(torch, w, steps, warmup, timer):
             t.grad = None
         o = m(q, k, v)
         o.backward(do)
-    ms, wall = timer.steps(step, steps, warmup)
-    log(f"[train512] step {ms:.4f} ms (wall {wall:.4f})")
-    return dict(ms=ms, wall_ms=wall)
+    # The backward on the calling thread: with the engine's per-device worker thread the
+    # step's host side (two thread hand-offs per backward) outlasts its GPU work.
+    with torch.autograd.set_multithreading_enabled(False):
+        ms, wall = timer.steps(step, steps, warmup)
+    ms_mt, wall_mt = timer.steps(step, steps, warmup)
+    log(f"[train512] step {ms:.4f} ms (wall {wall:.4f}); with the engine's worker thread {ms_mt:.4f} ms")
+    return dict(ms=ms, wall_ms=wall, autograd="backward on the calling thread (set_multithreading_enabled(False))",
+                ms_engine_worker_thread=ms_mt)
 
 
 def bench_sweep(torch, bam, wl, timer):
@@ -652,7 +657,8 @@ def main():
                 "workload": "autograd step through BamAttention at B=32 H=12 T=512 Dh=64: forward + backward, "
                             "grads for q, k, v, theta_alpha, theta_beta, theta_mu, s",
                 "ms": round(r["ms"], 4), "wall_ms": round(r["wall_ms"], 4),
-                "TFLOP/s": round(14.0 * 64 * 32 * 12 * 512 * 513 / 2 / r["ms"] / 1e9, 1)}
+                "TFLOP/s": round(14.0 * 64 * 32 * 12 * 512 * 513 / 2 / r["ms"] / 1e9, 1),
+                "autograd": r["autograd"], "ms_engine_worker_thread": round(r["ms_engine_worker_thread"], 4)}
         if cpu is not None:
             log("[cpu_baseline] training-shape forward + backward")
             cpu.fwdbwd_full(w3)
