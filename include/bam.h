@@ -324,11 +324,10 @@ bam_status bam_attn_decode_paged(const void* q, const void* k_pages, const void*
  * the per-row scalars with 32-bit byte ranges); BAM_EUNSUPPORTED otherwise.
  * Workspace (bam_bwd_workspace_size): the bias and derivative tables over the padded
  * distance range, four per-row fp32 scalars (D_i c_i / sqrt(Dh) among them) over rows
- * padded to 64, and
- * the per-head partial sums; contents are scratch between calls.  For T <= 512 and the
- * alpha or reference prior the kernels compute the bias and its derivatives themselves in
- * float32 (within a few float32 ulps of the tables' float64-derived values) and the
- * tables are not written.
+ * padded to 64, and the per-head partial sums; contents are scratch between calls.  For
+ * T <= 512 and the alpha or reference prior the kernels compute the bias and its
+ * derivatives themselves in float32 (within a few float32 ulps of the tables'
+ * float64-derived values) and the tables are not written.
  */
 size_t bam_bwd_workspace_size(int B, int H, int T, int Dh, unsigned flags);
 bam_status bam_attn_bwd(const void* q, const void* k, const void* v, const void* o, int o_dtype,
