@@ -105,3 +105,36 @@ def test_decode_split_invariance(L, Dh):
     for b in range(8):
         within(max_abs(o8[b], o1[0]), 1e-5 * max(1.0, float(np.max(np.abs(o1)))), f"O of sequence {b} vs B=1")
         within(max_abs(l8[b], l1[0]), 1e-5 * max(1.0, float(np.max(np.abs(l1)))), f"lse of sequence {b} vs B=1")
+
+
+@pytest.mark.parametrize("T,Dh,causal", [(300, 64, True), (700, 64, True), (200, 32, False)])
+def test_backward_with_constant_v(T, Dh, causal):
+    """V = 1 makes O = 1 whatever the weights, so nothing flows back to q, k or the prior's
+    parameters: with O = 1 passed in, dP_ij = sum_e dO_ie = D_i, so dZ = 0, dQ = dK = 0 and
+    dalpha = dbeta = ds = 0 up to float32 rounding of the two sums, while dV = P^T dO
+    (against the oracle).  The rounding bound: dQ and dK within 1e-3, and each parameter
+    gradient within 1e-3 of its head's conditioning scale for a random V."""
+    torch = torch_mod()
+    bam = _bam()
+    w = wl.random_case(5400 + T, 2, 3, T, Dh, "bf16", wl.CAUSAL * causal | wl.SSMAX, beta_range=(0.2, 1.2),
+                       with_grad=True)
+    p = params(w)
+    q, k, do = dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.do, "bf16")
+    ones = np.ones_like(w.v)
+    v = dev(ones, "bf16")
+    _, lse = bam.bam_attn_fwd(q, k, v, p["alpha"], p["beta"], p["mu"], p["s"], causal=causal, ssmax=True,
+                              o_dtype=torch.float32)
+    o = torch.ones(tuple(q.shape), dtype=torch.float32, device="cuda")
+    g = bam.bam_attn_bwd(q, k, v, o, lse, do, p["alpha"], p["beta"], p["mu"], p["s"], causal=causal, ssmax=True,
+                         grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    dq, dk, dv, da, db, ds = (host(x) for x in g)
+    within(float(np.max(np.abs(dq))), 1e-3, "max |dQ| with V = 1")
+    within(float(np.max(np.abs(dk))), 1e-3, "max |dK| with V = 1")
+    ref_v = oracle.attn_bwd(w.q, w.k, ones, w.do, w.alpha, w.beta, w.mu, w.s, causal=causal, ssmax=True)
+    within(max_abs(dv, ref_v["dv"]), 1e-2 * max(1.0, float(np.max(np.abs(ref_v["dv"])))), "dV = P^T dO with V = 1")
+    scale = oracle.attn_bwd(w.q, w.k, w.v, w.do, w.alpha, w.beta, w.mu, w.s, causal=causal, ssmax=True)
+    for name, x, A in (("dalpha", da, "A_alpha"), ("dbeta", db, "A_beta"), ("ds", ds, "A_s")):
+        r = np.abs(x) / (1e-3 * scale[A] + 1e-6)
+        h = int(np.argmax(r))
+        within(abs(float(x[h])), 1e-3 * float(scale[A][h]) + 1e-6, f"|{name}| with V = 1 (worst head {h})")
