@@ -65,3 +65,38 @@ def test_captured_fwd_decode_bwd_replays():
         ref = [ref_o, ref_l, ref_od, ref_ld] + list(ref_g)
         for i, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a, b), (rep, i)
+
+
+def test_graphed_training_module_replays():
+    """The autograd module under torch.cuda.make_graphed_callables (forward and backward
+    captured as graphs): over three replays with new q and dO, eager work in between, the
+    output and every gradient (q, k, v and the prior's parameters) equal the eager module's
+    bit for bit."""
+    torch = torch_mod()
+    from positional_prior_bias_amd.autograd import BamAttention
+    B, H, T, Dh = 2, 4, 300, 64
+    w = wl.random_case(2200, B, H, T, Dh, "bf16", wl.CAUSAL | wl.SSMAX, with_grad=True)
+    q0, k0, v0 = (dev(x, "bf16") for x in (w.q, w.k, w.v))
+    torch.manual_seed(0)
+    mod = BamAttention(H, max_seq_len=T, train_theta_mu=True, device="cuda")
+    sample = tuple(x.clone().requires_grad_(True) for x in (q0, k0, v0))
+    graphed = torch.cuda.make_graphed_callables(mod, sample)
+    gen = torch.Generator(device="cuda")
+    for rep in range(3):
+        gen.manual_seed(100 + rep)
+        qn = torch.randn(q0.shape, device="cuda", generator=gen).to(torch.bfloat16)
+        dn = torch.randn(q0.shape, device="cuda", generator=gen).to(torch.bfloat16)
+        res = []
+        for fn in (graphed, mod):
+            x = [t.clone().requires_grad_(True) for t in (qn, k0, v0)]
+            for prm in mod.parameters():
+                prm.grad = None
+            out = fn(*x)
+            out.backward(dn)
+            torch.cuda.synchronize()
+            res.append([out.detach().clone()] + [t.grad.clone() for t in x]
+                       + [prm.grad.clone() for prm in mod.parameters() if prm.grad is not None])
+            _ = (torch.randn(1 << 20, device="cuda") * 2).sum().item()
+        assert len(res[0]) == len(res[1]) == 8, (len(res[0]), len(res[1]))
+        for i, (a, b) in enumerate(zip(res[0], res[1])):
+            assert torch.equal(a, b), (rep, i)
