@@ -388,15 +388,19 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
     u32x4 pf[NQB][4];
 #pragma unroll
     for (int qb2 = 0; qb2 < NQB; ++qb2) {
-      float mxa = kNegInf, mxb = kNegInf;
+      // the 32 values of the lane as a tree of three-input maxima: 16 instructions
+      float v[32], t1[11], t2[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; x += 4) {
-          mxa = max3(mxa, sacc[qb2][kb][x], sacc[qb2][kb][x + 1]);
-          mxb = max3(mxb, sacc[qb2][kb][x + 2], sacc[qb2][kb][x + 3]);
-        }
-      const float mx = max_xor32(__builtin_fmaxf(mxa, mxb));
+        for (int x = 0; x < 16; ++x) v[16 * kb + x] = sacc[qb2][kb][x];
+#pragma unroll
+      for (int i = 0; i < 10; ++i) t1[i] = max3(v[3 * i], v[3 * i + 1], v[3 * i + 2]);
+      t1[10] = __builtin_fmaxf(v[30], v[31]);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) t2[i] = max3(t1[3 * i], t1[3 * i + 1], t1[3 * i + 2]);
+      t2[3] = max3(t1[9], t1[10], t2[2]);
+      const float mx = max_xor32(max3(t2[0], t2[1], t2[3]));
       // The running max is exact (not lazy): the largest weight computed so far is then
       // exactly 1 and every weight is at most 1, so rounding P to bf16 perturbs each weight
       // by at most 2^-8 of itself.  (A lazy max that moved only on jumps of 2^8 let the
