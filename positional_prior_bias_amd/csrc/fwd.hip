@@ -437,7 +437,8 @@ __global__ void __launch_bounds__(256, (DH == 64 && NQB == 1) ? 4 : 2) fwd_bf16_
           const float p0 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x], -m_use));
           const float p1 = exp2_fast(fmaf(Cl[qb2], sacc[qb2][kb][x + 1], -m_use));
           pf[qb2][2 * kb + (x >> 3)][(x & 7) >> 1] = pack_bf16x2(p0, p1);
-          ls += p0 + p1;
+          // the first pair starts the sum (0 + y is not folded away for a float y)
+          ls = (kb == 0 && x == 0) ? p0 + p1 : ls + (p0 + p1);
         }
       l[qb2] += ls;
     }
